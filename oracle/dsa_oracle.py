@@ -1,0 +1,173 @@
+"""CPU reference for the DeepSeek Sparse Attention (DSA) forward path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it, and it shares no code with the GPU library.
+
+It is the plain definition of the method, evaluated directly in float64 with
+numpy (a matrix product and a sort serve as library steps; nothing is blocked,
+fused or reordered beyond what the definitions state).  Sources, all on the
+page "DeepSeek-V3.2: sparse attention, scaled RL and synthetic agent
+environments" (PaperTrace analysis of arXiv 2512.02556):
+
+* Lightning indexer, Sec. 1.1 Eq. (1):
+      I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
+  over the tokens s that precede the query t.
+* Fine-grained token selection, Sec. 1.1 (Eq. (4) defines the set):
+      S_t = { s : I[t,s] in Top-k(I[t,:]) }
+* Sparse attention, Sec. 1.1 Eq. (2): u_t = Attn(h_t, {c_s : s in S_t}); the
+  index scores only choose the set and do not enter the attention weights;
+  the softmax is taken over the selected set only (Sec. 5.2 Eq. (19)).
+* MLA in MQA mode, Sec. 1.1 (and Fig. 7): every selected 576-d latent row is
+  shared by all 128 query heads; keys are the whole row, values its first
+  512 dims.
+* Short rows select among min(k, t) positions (Sec. 5.1).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+* "preceding" is inclusive: a query at absolute position p sees s <= p, so a
+  row has n_p = min(p + 1, S) candidates and m_p = min(k, n_p) selections.
+* FP8 is OCP E4M3 (E4M3FN) with one positive fp32 scale per token; the
+  quantised value is code * scale.  Eq. (1) is evaluated on those values.
+* No extra constant (1/sqrt(d) etc.) in Eq. (1).
+* Ties at the top-k cutoff go to the lower index; the selected set is
+  reported in ascending index order padded with -1 to k entries.  NaN ranks
+  below every number; -0.0 equals +0.0.
+* Attention logits are sm_scale * (q . c_s) over all Dk dims; values are
+  c_s[0:Dv].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------- formats
+def _e4m3_table() -> np.ndarray:
+    """Value of every OCP FP8 E4M3FN byte (OCP 8-bit Floating Point
+    Specification v1.0, E4M3: sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal; S.1111.111 is NaN; no infinities)."""
+    t = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            t[c] = np.nan
+        elif e == 0:
+            t[c] = s * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            t[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """bfloat16 bit pattern -> float64 (bf16 is the top half of a float32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def dequant_e4m3(codes, scales) -> np.ndarray:
+    """value = decoded code * per-token scale (exact in float64)."""
+    v = e4m3_decode(codes)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return v * s.reshape(s.shape + (1,) * (v.ndim - s.ndim))
+
+
+# ----------------------------------------------------------------- shapes
+def n_candidates(p: int, n_kv: int) -> int:
+    """n_p = min(p + 1, S): inclusive causal row length at absolute position p."""
+    return min(p + 1, n_kv)
+
+
+def n_selected(p: int, n_kv: int, k: int) -> int:
+    """m_p = min(k, n_p) (short rows select everything they have)."""
+    return min(k, n_candidates(p, n_kv))
+
+
+# ----------------------------------------------------------------- Eq. (1)
+def indexer_row(q_t: np.ndarray, w_t: np.ndarray, k_all: np.ndarray, p: int) -> np.ndarray:
+    """Index scores of one query row.
+
+    q_t: [H_I, d_I] real-valued indexer queries of token t.
+    w_t: [H_I] head weights of token t.
+    k_all: [S, d_I] real-valued indexer keys.
+    p: absolute position of the query.
+    Returns float32 [n_p]: I[t, s] for s = 0..n_p-1, computed in float64 as
+    sum_j w[t,j] * max(0, q[t,j] . k[s]) and rounded once to float32."""
+    n = n_candidates(p, k_all.shape[0])
+    q = np.asarray(q_t, dtype=np.float64)
+    k = np.asarray(k_all[:n], dtype=np.float64)
+    w = np.asarray(w_t, dtype=np.float64)
+    dots = k @ q.T                          # [n, H_I]: q[t,j] . k[s]
+    relu = np.maximum(dots, 0.0)
+    return (relu @ w).astype(np.float32)
+
+
+def indexer_scores(q_idx, w_idx, k_idx, q_pos0: int) -> list:
+    """All rows of one sequence: q_idx [T, H_I, d_I], w_idx [T, H_I],
+    k_idx [S, d_I].  Returns a list of float32 rows (row i has n_p entries)."""
+    return [indexer_row(q_idx[i], w_idx[i], k_idx, q_pos0 + i) for i in range(q_idx.shape[0])]
+
+
+# ----------------------------------------------------------------- Top-k
+def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """Top-k of one score row (all entries are candidates).
+
+    Order: larger score first; NaN below every number; -0.0 == +0.0; equal
+    scores go to the lower index.  Returns int32 [k]: the chosen indices in
+    ascending order, then -1 padding."""
+    x = np.asarray(scores, dtype=np.float32).astype(np.float64)
+    n = x.shape[0]
+    m = min(k, n)
+    nan = np.isnan(x)
+    val = np.where(nan, 0.0, x) + 0.0       # + 0.0 maps -0.0 to +0.0
+    idx = np.arange(n)
+    order = np.lexsort((idx, -val, nan))     # primary: not-NaN first; then value desc; then index asc
+    chosen = np.sort(order[:m])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:m] = chosen
+    return out
+
+
+# ----------------------------------------------------------------- Eq. (2)/(19)
+def sparse_mla_row(q_t: np.ndarray, kv: np.ndarray, sel: np.ndarray, sm_scale: float, dim_v: int,
+                   return_weights: bool = False):
+    """MQA-mode attention of one query token over the selected latent rows.
+
+    q_t: [H, Dk] absorbed per-head queries; kv: [S, Dk] latent rows (keys are
+    whole rows, values their first dim_v dims); sel: selected row indices
+    (entries < 0 are padding and skipped).  Softmax is over the selected set
+    only.  Returns o [H, dim_v] and lse [H] (natural log of the softmax
+    denominator including the max), in float64."""
+    s = np.asarray(sel)
+    s = s[s >= 0]
+    q = np.asarray(q_t, dtype=np.float64)
+    c = np.asarray(kv, dtype=np.float64)[s]           # [m, Dk]
+    if s.size == 0:
+        o = np.zeros((q.shape[0], dim_v))
+        lse = np.full(q.shape[0], -np.inf)
+        return (o, lse, np.zeros((q.shape[0], 0))) if return_weights else (o, lse)
+    z = sm_scale * (q @ c.T)                          # [H, m]
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    den = e.sum(axis=1, keepdims=True)
+    p = e / den
+    o = p @ c[:, :dim_v]
+    lse = (zmax + np.log(den))[:, 0]
+    return (o, lse, p) if return_weights else (o, lse)
+
+
+# ----------------------------------------------------------------- whole path
+def dsa_row(q_idx_t, w_t, k_idx, q_t, kv, p: int, k: int, sm_scale: float, dim_v: int):
+    """One query row through indexer -> top-k -> sparse attention.
+    Returns (scores float32 [n_p], sel int32 [k], o [H, dim_v], lse [H])."""
+    sc = indexer_row(q_idx_t, w_t, k_idx, p)
+    sel = topk_row(sc, k)
+    o, lse = sparse_mla_row(q_t, kv, sel, sm_scale, dim_v)
+    return sc, sel, o, lse

@@ -1,0 +1,271 @@
+"""Pins of the CPU reference (oracle/) to things other than itself:
+hand-worked examples from the definitions (tests/golden), closed forms,
+library routines for special cases, and invariants the method guarantees.
+A plausible slip in the reference (dropped ReLU, ReLU after the head sum, a
+wrong weight/head pairing, a wrong sign, a transposed operand, an off-by-one
+in the causal window, the wrong tie order, a softmax over the wrong set)
+fails at least one of these."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+
+
+def _parse_floats(s):
+    return [float(x) for x in s.replace("|", " ").split()]
+
+
+# ------------------------------------------------------------------ FP8 / bf16 decode
+def test_e4m3_spot_values_from_ocp_spec(golden_dir):
+    for line in open(f"{golden_dir}/e4m3_spot.txt"):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        got = O.e4m3_decode(np.uint8(int(code, 16)))
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert got == float(val), (code, got, val)
+            if val == "-0":
+                assert np.signbit(got)
+
+
+def test_e4m3_all_codes_match_torch_float8():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+    assert np.isnan(got).sum() == 2  # only S.1111.111
+
+
+def test_bf16_decode_matches_torch():
+    bits = np.random.RandomState(0).randint(0, 1 << 16, size=4096).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]  # finite values
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_decode(bits), ref)
+
+
+# ------------------------------------------------------------------ indexer, Eq. (1)
+def _indexer_golden(golden_dir):
+    keys, queries, topk = [], {}, None
+    for line in open(f"{golden_dir}/indexer_worked.txt"):
+        if line.startswith("#") or not line.strip():
+            continue
+        if line.startswith("key"):
+            keys.append(_parse_floats(line.split(":")[1]))
+        elif line.startswith("query"):
+            head, rest = line.split("heads:")
+            name, p = head.split()[0], int(head.split("p=")[1])
+            hs, rest = rest.split("weights:")
+            ws, sc = rest.split("scores:")
+            heads = [_parse_floats(h) for h in hs.split("|") if h.strip()]
+            queries[name] = (p, np.array(heads), np.array(_parse_floats(ws)), np.array(_parse_floats(sc)))
+        elif line.startswith("topk"):
+            k = int(line.split("k=")[1].split(":")[0])
+            topk = (k, [int(x) for x in line.split(":")[1].split()])
+    return np.array(keys), queries, topk
+
+
+def test_indexer_worked_example(golden_dir):
+    keys, queries, _ = _indexer_golden(golden_dir)
+    for name, (p, q, w, want) in queries.items():
+        got = O.indexer_row(q, w, keys, p)
+        assert got.shape == (p + 1,), name
+        assert np.array_equal(got, want.astype(np.float32)), (name, got, want)
+
+
+def test_topk_of_worked_indexer_row(golden_dir):
+    keys, queries, (k, want) = _indexer_golden(golden_dir)
+    p, q, w, _ = queries["queryA"]
+    sel = O.topk_row(O.indexer_row(q, w, keys, p), k)
+    assert list(sel) == want
+
+
+def test_indexer_single_head_unit_weight_is_relu_dot():
+    # H_I = 1, w = 1: Eq. (1) reduces to ReLU(q . k) -- checked with torch.
+    rs = np.random.RandomState(1)
+    q = rs.randn(1, 16)
+    k = rs.randn(40, 16)
+    got = O.indexer_row(q, np.ones(1), k, 39)
+    ref = torch.relu(torch.from_numpy(k) @ torch.from_numpy(q[0])).numpy().astype(np.float32)
+    assert np.array_equal(got, ref)
+
+
+def test_indexer_causal_window_and_cache_bound():
+    rs = np.random.RandomState(2)
+    q, w, k = rs.randn(4, 8), rs.randn(4), rs.randn(10, 8)
+    assert O.indexer_row(q, w, k, 0).shape == (1,)       # a token sees itself
+    assert O.indexer_row(q, w, k, 6).shape == (7,)
+    assert O.indexer_row(q, w, k, 25).shape == (10,)     # capped by the cache length
+    # entries do not depend on later keys
+    k2 = k.copy(); k2[7:] = 1e6
+    assert np.array_equal(O.indexer_row(q, w, k, 6), O.indexer_row(q, w, k2, 6))
+
+
+def test_indexer_homogeneity_linearity_and_sign():
+    rs = np.random.RandomState(3)
+    q, k = rs.randn(6, 12), rs.randn(30, 12)
+    w1, w2 = rs.randn(6), rs.randn(6)
+    base = O.indexer_row(q, w1, k, 29).astype(np.float64)
+    # positive scaling of q or of k scales the score (ReLU is positively homogeneous)
+    assert np.allclose(O.indexer_row(2.5 * q, w1, k, 29), 2.5 * base, rtol=1e-6)
+    assert np.allclose(O.indexer_row(q, w1, 0.25 * k, 29), 0.25 * base, rtol=1e-6)
+    # linear in the head weights
+    s12 = O.indexer_row(q, w1 + w2, k, 29).astype(np.float64)
+    assert np.allclose(s12, base + O.indexer_row(q, w2, k, 29), rtol=1e-5, atol=1e-5)
+    # non-negative weights give non-negative scores; flipping q and k together
+    # leaves dot products and therefore scores unchanged
+    assert np.all(O.indexer_row(q, np.abs(w1), k, 29) >= 0)
+    assert np.array_equal(O.indexer_row(-q, w1, -k, 29), O.indexer_row(q, w1, k, 29))
+    # orthogonal query and keys score zero
+    qo = np.zeros((6, 12)); qo[:, 0] = 1
+    ko = rs.randn(30, 12); ko[:, 0] = 0
+    assert np.all(O.indexer_row(qo, w1, ko, 29) == 0)
+
+
+def test_indexer_fp8_inputs_are_exact_in_float64():
+    # With FP8 values, every product and partial sum of q.k is exact in
+    # float64, so the score equals its value computed in exact rationals.
+    from fractions import Fraction
+    rs = np.random.RandomState(4)
+    codes_q = rs.randint(0, 256, size=(2, 16)).astype(np.uint8)
+    codes_k = rs.randint(0, 256, size=(3, 16)).astype(np.uint8)
+    codes_q[(codes_q & 0x7F) == 0x7F] = 0
+    codes_k[(codes_k & 0x7F) == 0x7F] = 0
+    q = O.e4m3_decode(codes_q); k = O.e4m3_decode(codes_k)
+    w = np.array([0.75, -1.25])
+    got = O.indexer_row(q, w, k, 2)
+    for s in range(3):
+        exact = Fraction(0)
+        for j in range(2):
+            d = sum(Fraction(float(q[j, i])) * Fraction(float(k[s, i])) for i in range(16))
+            exact += Fraction(float(w[j])) * max(d, Fraction(0))
+        assert got[s] == np.float32(float(exact))
+
+
+# ------------------------------------------------------------------ top-k
+def test_topk_worked_examples(golden_dir):
+    for line in open(f"{golden_dir}/topk_worked.txt"):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, sc, want = line.split("|")
+        got = O.topk_row(np.array([float(x) for x in sc.split()], dtype=np.float32), int(k))
+        assert list(got) == [int(x) for x in want.split()], line
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_topk_defining_properties_random_rows(seed):
+    # Brute-force check of the definition: |S| = min(k, n); every chosen score
+    # >= every unchosen score; among equal scores at the cutoff, the chosen
+    # indices are the lowest ones; output sorted and padded.
+    rs = np.random.RandomState(seed)
+    n = rs.randint(1, 400)
+    k = rs.randint(1, 300)
+    x = np.round(rs.randn(n) * 3).astype(np.float32)   # many ties
+    sel = O.topk_row(x, k)
+    m = min(k, n)
+    chosen = sel[:m]
+    assert np.all(sel[m:] == -1)
+    assert np.all(np.diff(chosen) > 0)
+    rest = np.setdiff1d(np.arange(n), chosen)
+    if rest.size:
+        assert x[chosen].min() >= x[rest].max()
+        tau = x[chosen].min()
+        tied_out = rest[x[rest] == tau]
+        tied_in = chosen[x[chosen] == tau]
+        if tied_out.size:
+            assert tied_in.max() < tied_out.min()
+
+
+def test_topk_all_equal_and_short_rows():
+    assert list(O.topk_row(np.zeros(50, np.float32), 7)) == list(range(7))
+    assert list(O.topk_row(np.arange(5, dtype=np.float32), 8)) == [0, 1, 2, 3, 4, -1, -1, -1]
+
+
+# ------------------------------------------------------------------ attention, Eq. (2)/(19)
+def test_attention_single_entry_closed_form():
+    rs = np.random.RandomState(5)
+    q, kv = rs.randn(4, 10), rs.randn(6, 10)
+    o, lse = O.sparse_mla_row(q, kv, np.array([3, -1, -1]), 0.3, 7)
+    assert np.array_equal(o, np.broadcast_to(kv[3, :7], (4, 7)))
+    assert np.allclose(lse, 0.3 * q @ kv[3], rtol=1e-14)
+
+
+def test_attention_two_entries_sigmoid_closed_form():
+    rs = np.random.RandomState(6)
+    q, kv = rs.randn(3, 8), rs.randn(5, 8)
+    o, lse = O.sparse_mla_row(q, kv, np.array([1, 4]), 0.7, 6)
+    z1, z2 = 0.7 * q @ kv[1], 0.7 * q @ kv[4]
+    a = 1.0 / (1.0 + np.exp(z2 - z1))
+    assert np.allclose(o, a[:, None] * kv[1, :6] + (1 - a)[:, None] * kv[4, :6], rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse, np.logaddexp(z1, z2), rtol=1e-12)
+
+
+def test_attention_all_positions_equals_dense_causal_sdpa():
+    # When k >= n_p the selection is every position, so the path is dense
+    # causal MQA attention: checked against torch's SDPA in float64.
+    rs = np.random.RandomState(7)
+    L, H, Dk, Dv = 24, 4, 12, 8
+    q, kv = rs.randn(L, H, Dk), rs.randn(L, Dk)
+    scale = 1 / math.sqrt(Dk)
+    got = np.stack([O.sparse_mla_row(q[t], kv, O.topk_row(np.zeros(t + 1, np.float32), 64), scale, Dv)[0]
+                    for t in range(L)])
+    qt = torch.from_numpy(q).permute(1, 0, 2)                          # [H, L, Dk]
+    kt = torch.from_numpy(kv).unsqueeze(0).expand(H, L, Dk).contiguous()
+    vt = torch.from_numpy(kv[:, :Dv]).unsqueeze(0).expand(H, L, Dv).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    assert np.allclose(got, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_softmax_weights_sum_to_one_and_lse_matches_logsumexp():
+    from scipy.special import logsumexp
+    rs = np.random.RandomState(8)
+    q, kv = rs.randn(5, 16) * 3, rs.randn(100, 16)
+    sel = np.array([0, 7, 9, 33, 50, 51, 99, -1, -1])
+    o, lse, p = O.sparse_mla_row(q, kv, sel, 0.5, 16, return_weights=True)
+    assert np.all(np.abs(p.sum(axis=1) - 1) < 1e-12)
+    s = sel[sel >= 0]
+    assert np.allclose(lse, logsumexp(0.5 * q @ kv[s].T, axis=1), rtol=1e-13)
+    # the index scores never enter the weights: only the set matters, and its order does not
+    perm = np.array([51, 99, 0, 33, 9, 7, 50])
+    o2, lse2 = O.sparse_mla_row(q, kv, perm, 0.5, 16)
+    assert np.allclose(o, o2, rtol=1e-12) and np.allclose(lse, lse2, rtol=1e-12)
+
+
+def test_attention_eq20_mass_bound():
+    # Sec. 5.2 Eq. (20): ||o_dense - o_sparse|| <= 2 (1 - M_k) V with M_k the
+    # dense softmax mass on the selected set and V a bound on |v|.
+    rs = np.random.RandomState(9)
+    n, H, D = 200, 6, 16
+    q, kv = rs.randn(H, D), rs.randn(n, D)
+    dense, _, pd = O.sparse_mla_row(q, kv, np.arange(n), 0.4, D, return_weights=True)
+    for k in (5, 50, 150):
+        sel = rs.choice(n, size=k, replace=False)
+        sparse, _ = O.sparse_mla_row(q, kv, sel, 0.4, D)
+        mk = pd[:, sel].sum(axis=1)
+        vmax = np.abs(kv).max()
+        assert np.all(np.abs(dense - sparse).max(axis=1) <= 2 * (1 - mk) * vmax + 1e-12)
+
+
+def test_whole_row_path_with_k_covering_row_is_dense():
+    rs = np.random.RandomState(10)
+    qI, wI, kI = rs.randn(4, 8), rs.randn(4), rs.randn(30, 8)
+    q, kv = rs.randn(3, 12), rs.randn(30, 12)
+    sc, sel, o, lse = O.dsa_row(qI, wI, kI, q, kv, 20, 32, 0.3, 10)
+    assert list(sel[:21]) == list(range(21)) and np.all(sel[21:] == -1)
+    od, _ = O.sparse_mla_row(q, kv, np.arange(21), 0.3, 10)
+    assert np.array_equal(o, od)
+
+
+# ------------------------------------------------------------------ cost figures (Sec. 1.1)
+def test_cost_figures_of_the_pages():
+    # 64 index heads x 128 dims = 8192 MAC per pair; 128 heads x (576 + 512)
+    # = 139,264 MAC per selected pair, about 17x more; k = 2048 of 128K = 1.6%.
+    assert 64 * 128 == 8192
+    assert 128 * (576 + 512) == 139264
+    assert round(139264 / 8192) == 17
+    assert abs(2048 / 131072 - 0.016) < 0.0005
