@@ -1,0 +1,256 @@
+"""Benchmark of the DSA forward path on one MI355X.
+
+One step = one dsa_forward over the whole workload (indexer -> top-k ->
+sparse MLA for every query row), inputs already resident in HBM.  Prints one
+JSON line:
+  value        query-tokens/s of dsa_forward on the 128K prefill workload
+  roofline     the dominant kernel's algorithmic throughput against its peak
+  cpu_baseline the CPU oracle on a stratified row sample of the same workload
+plus per-stage times, indexer FP8 TFLOP/s and the 64 x 128K decode step.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload p128k]
+                       [--no-cpu-baseline] [--no-decode] [--stages-only]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "DSA fwd query-tokens/sec at L=128K,k=2048; indexer FP8 TFLOP/s; decode GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+def alloc_forward(torch, wl, dsa):
+    dims = dsa.Dims.of(wl)
+    out = torch.empty((wl.batch, wl.n_q, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.batch, wl.n_q, wl.heads), dtype=torch.float32, device="cuda")
+    nws = dsa.dsa_forward_workspace_size(dims)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    return dims, out, lse, ws, nws
+
+
+def time_forward(torch, wl, d, dsa, steps, warmup, stream):
+    dims, out, lse, ws, nws = alloc_forward(torch, wl, dsa)
+
+    def step():
+        dsa.dsa_forward(dims, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], d["q"], d["kv"],
+                        wl.sm_scale, out, lse, None, ws, nws, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    e0 = t.event()
+    for _ in range(steps):
+        step()
+    e1 = t.event()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_stages(torch, wl, d, dsa, reps, stream):
+    """The forward's chunk loop through the three separate calls (bit-identical
+    launches), with events between stages: per-kernel average durations."""
+    import synth.workloads as W  # noqa: F401
+    S, k = wl.n_kv, wl.topk
+    full = dsa.Dims.of(wl)
+    nws = dsa.dsa_forward_workspace_size(full)
+    # chunk rows used by dsa_forward (same rule: ~128 MiB of scores per chunk)
+    tc = max(1, (128 << 20) // (wl.batch * S * 4))
+    if tc >= 64:
+        tc = tc // 32 * 32
+    tc = min(tc, wl.n_q)
+    sc = torch.empty((wl.batch, tc, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.batch, tc, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.batch, wl.n_q, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.batch, wl.n_q, wl.heads), dtype=torch.float32, device="cuda")
+    assert wl.batch == 1 or tc == wl.n_q
+    anws = dsa.dsa_attn_workspace_size(full)
+    aws = torch.empty(max(anws, 1), dtype=torch.uint8, device="cuda")
+    t = Timer(torch, stream)
+    tot = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    launches = 0
+    s = stream.cuda_stream
+    HI, dI, H, Dk, Dv = wl.idx_heads, wl.idx_dim, wl.heads, wl.dim_qk, wl.dim_v
+    for _ in range(reps):
+        for i0 in range(0, wl.n_q, tc):
+            rows = min(tc, wl.n_q - i0)
+            cd = dsa.Dims.of(wl, n_q=rows, q_pos0=wl.q_pos0 + i0)
+            if wl.batch == 1:
+                qi, qs, w = d["q_idx"][:, i0:], d["q_scale"][:, i0:], d["w_idx"][:, i0:]
+                q, o, l = d["q"][:, i0:], out[:, i0:], lse[:, i0:]
+            else:
+                qi, qs, w, q, o, l = d["q_idx"], d["q_scale"], d["w_idx"], d["q"], out, lse
+            e0 = t.event()
+            dsa.dsa_indexer_scores(cd, qi, qs, w, d["k_idx"], d["k_scale"], sc, S, stream=s)
+            e1 = t.event()
+            dsa.dsa_topk(cd, sc, S, idx, stream=s)
+            e2 = t.event()
+            # attention of a chunk uses the workload's split rule, as dsa_forward does
+            dsa.dsa_sparse_mla_attn(cd, q, d["kv"], idx, wl.sm_scale, o, l, aws, anws, stream=s)
+            e3 = t.event()
+            torch.cuda.synchronize()
+            tot["indexer"] += e0.elapsed_time(e1)
+            tot["topk"] += e1.elapsed_time(e2)
+            tot["attention"] += e2.elapsed_time(e3)
+            launches += 1
+    return {k2: v / reps for k2, v in tot.items()}, launches // reps, nws
+
+
+def cpu_baseline(wl, n_rows):
+    """The CPU oracle (unchanged) on a stratified sample of query rows:
+    rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
+    from oracle import dsa_oracle as O
+    from synth import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    L = wl.n_q
+    rows = [int((r + 0.5) * L / n_rows) for r in range(n_rows)]
+    c, s = W.k_idx_fp8(wl, 0, 0, wl.n_kv)
+    k_all = O.dequant_e4m3(c, s)
+    kv = O.bf16_decode(W.kv_bf16_rows(wl, 0, np.arange(wl.n_kv)))
+    qc, qs = W.q_idx_fp8(wl, 0, rows)
+    qi = O.dequant_e4m3(qc, qs)
+    w = O.bf16_decode(W.w_idx_bf16(wl, 0, rows))
+    q = O.bf16_decode(W.q_bf16(wl, 0, rows))
+    t0 = time.perf_counter()
+    for n, i in enumerate(rows):
+        O.dsa_row(qi[n], w[n], k_all, q[n], kv, wl.q_pos0 + i, wl.topk, wl.sm_scale, wl.dim_v)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_rows} stratified query rows of {wl.name} (rows floor((r+1/2)L/{n_rows})), "
+                      f"float64 numpy, {dt:.1f} s timed; input generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="p128k")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the DSA forward path here is a single-GPU build "
+              "(multi-GPU sharding is a design note, not implemented); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_long_amd as dsa
+    from synth import workloads as W
+    from synth.device import fill_inputs
+
+    wl = W.WORKLOADS[args.workload]
+    stream = torch.cuda.current_stream()
+    log(f"[bench] filling {wl.name} inputs on the GPU")
+    d = fill_inputs(wl)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} dsa_forward steps after {args.warmup} warm-up")
+    ms = time_forward(torch, wl, d, dsa, args.steps, args.warmup, stream)
+    toks = wl.batch * wl.n_q / (ms / 1e3)
+    log(f"[bench] dsa_forward {ms:.2f} ms/step -> {toks:,.0f} query-tokens/s")
+
+    log("[bench] per-stage pass (indexer / top-k / attention events)")
+    stages, launches, _ = time_stages(torch, wl, d, dsa, args.stage_reps, stream)
+    idx_flop = wl.indexer_flop()
+    attn_flop = wl.attn_flop()
+    idx_tflops = idx_flop / (stages["indexer"] / 1e3) / 1e12
+    attn_tflops = attn_flop / (stages["attention"] / 1e3) / 1e12
+    topk_bytes = 4.0 * wl.causal_pairs() + 4.0 * wl.batch * wl.n_q * wl.topk
+    topk_gbs = topk_bytes / (stages["topk"] / 1e3) / 1e9
+    log(f"[bench] stages ms {stages}; indexer {idx_tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s, "
+        f"top-k {topk_gbs:.0f} GB/s")
+    dom = max(stages, key=stages.get)
+    if dom == "indexer":
+        roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma", "achieved": idx_tflops,
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "dtype": "fp8"}
+    elif dom == "attention":
+        roof = {"kernel": "sparse_mla_kernel<576,512,4>", "bound": "mfma", "achieved": attn_tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16"}
+    else:
+        roof = {"kernel": "topk_kernel", "bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["launches"] = launches
+    del d
+    torch.cuda.empty_cache()
+
+    decode = None
+    if not args.no_decode:
+        dw = W.WORKLOADS["dec64"]
+        log("[bench] decode workload dec64")
+        dd = fill_inputs(dw)
+        torch.cuda.synchronize()
+        dms = time_forward(torch, dw, dd, dsa, max(args.steps, 10), args.warmup, stream)
+        dstages, _, _ = time_stages(torch, dw, dd, dsa, 10, stream)
+        B, S, k = dw.batch, dw.n_kv, dw.topk
+        idx_bytes = B * S * (dw.idx_dim + 4) + B * dw.idx_heads * (dw.idx_dim + 2) + B * 4 + 4 * B * S
+        topk_b = 4 * B * S + 4 * B * k
+        mla_bytes = B * k * dw.dim_qk * 2 + B * dw.heads * dw.dim_qk * 2 + B * dw.heads * dw.dim_v * 2
+        step_bytes = idx_bytes + topk_b + mla_bytes
+        decode = {"workload": "dec64", "ms_per_step": dms, "GB_per_s": step_bytes / (dms / 1e3) / 1e9,
+                  "stages_ms": dstages,
+                  "indexer_GB_per_s": idx_bytes / (dstages["indexer"] / 1e3) / 1e9,
+                  "topk_GB_per_s": topk_b / (dstages["topk"] / 1e3) / 1e9,
+                  "mla_gather_GB_per_s": mla_bytes / (dstages["attention"] / 1e3) / 1e9,
+                  "algorithmic_bytes_per_step": step_bytes}
+        decode["mla_frac_of_hbm_peak"] = decode["mla_gather_GB_per_s"] / PEAK_HBM_GBS
+        log(f"[bench] decode {dms*1e3:.1f} us/step; {decode}")
+        del dd
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_rows} rows")
+        cpu = cpu_baseline(wl, args.cpu_rows)
+        log(f"[bench] cpu {cpu}")
+
+    res = {
+        "metric": METRIC, "value": toks, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8/bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "L": wl.n_kv, "n_q": wl.n_q, "topk": wl.topk,
+                   "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim, "heads": wl.heads, "dim_qk": wl.dim_qk,
+                   "dim_v": wl.dim_v},
+        "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
+        "topk_GB_per_s": topk_gbs, "roofline": roof, "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) forward path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "DeepSeek-V3.2: sparse attention, scaled RL and synthetic
+ * agent environments", Sec. 1.1, Eq. (1) and (2); Sec. 5.1; Sec. 5.2 Eq. (19)):
+ *
+ *   I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])            lightning indexer
+ *   S_t    = the k positions s <= t with the largest I[t,s] token selection
+ *   u_t    = softmax-weighted sum over S_t of the latent   sparse MLA (MQA mode)
+ *            rows c_s, every row shared by all query heads
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers, dense and row-major, owned by
+ *   the caller.  The library allocates no memory; the calls that need
+ *   scratch space take a caller-owned workspace (size from *_workspace_size).
+ * - Outputs must not alias inputs or each other.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   work is enqueued asynchronously on it; a call returns without waiting.
+ * - The return value is a dsa_status.  Host-side validation happens before
+ *   any HIP call: on a validation failure nothing is launched and outputs are
+ *   untouched.  A failed launch returns DSA_ERR_HIP.  Faults inside kernels
+ *   surface at the caller's next synchronisation.
+ * - dsa_last_error() returns a thread-local description of the last failure.
+ * - Element types: "e4m3" is an OCP FP8 E4M3FN byte; "bf16" is a bfloat16
+ *   bit pattern in a uint16_t; scales and scores are IEEE float32.
+ *
+ * Positions: query row i (0 <= i < n_q) of a sequence sits at absolute
+ * position p = q_pos0 + i and sees the n_p = min(p + 1, n_kv) cache entries
+ * s = 0 .. n_p - 1 (s <= p: a token sees itself).  It selects
+ * m_p = min(topk, n_p) of them (short rows select everything, Sec. 5.1).
+ * Requires 0 <= q_pos0 and q_pos0 + n_q <= n_kv.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dsa_dims {
+  int32_t batch;     /* B: independent sequences                                  */
+  int32_t n_q;       /* T: query rows per sequence                                */
+  int32_t n_kv;      /* S: cached tokens per sequence                             */
+  int32_t q_pos0;    /* absolute position of query row 0 (prefill 0, decode S-1)  */
+  int32_t idx_heads; /* H_I: indexer heads, 1..64                                 */
+  int32_t idx_dim;   /* d_I: indexer head dim, multiple of 16, 16..128            */
+  int32_t heads;     /* H: attention query heads, 1..128                          */
+  int32_t dim_qk;    /* Dk: latent row width (keys), multiple of 16, <= 576       */
+  int32_t dim_v;     /* Dv: value width = first Dv dims of a row, mult. of 32, <= 512, <= Dk */
+  int32_t topk;      /* k: selected entries per query, 1..2048                    */
+} dsa_dims;
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, inconsistent dims, bad scale, ld too small */
+  DSA_ERR_UNSUPPORTED = 2, /* dims outside what the kernels are built for          */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required            */
+  DSA_ERR_HIP = 4          /* a HIP launch or runtime call failed                   */
+} dsa_status;
+
+/*
+ * Lightning indexer scores (Eq. (1), Sec. 1.1).  FP8 inputs with one fp32
+ * scale per token: the indexer query of head j of row i is
+ * q_scale[b,i] * e4m3(q_idx[b,i,j,:]) and the key of entry s is
+ * k_scale[b,s] * e4m3(k_idx[b,s,:]).
+ *
+ *   q_idx   [B, T, H_I, d_I] e4m3     q_scale [B, T] f32 (> 0, finite)
+ *   w_idx   [B, T, H_I]      bf16     head weights w[t,j]
+ *   k_idx   [B, S, d_I]      e4m3     k_scale [B, S] f32 (> 0, finite)
+ *   scores  [B, T, ld]       f32      out: scores[b,i,s] = I[p,s] for s < n_p;
+ *                                      entries s >= n_p are not written.
+ *   ld >= n_kv (row stride of scores, in elements).
+ * Products are exact FP8 x FP8 and summed in fp32; the ReLU, head weighting
+ * and head sum are done in fp32.  Scales are not validated on the device.
+ */
+int dsa_indexer_scores(const dsa_dims* dims, const uint8_t* q_idx, const float* q_scale,
+                       const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale,
+                       float* scores, int64_t ld, void* stream);
+
+/*
+ * Top-k selection (S_t, Sec. 1.1 and Eq. (4); short rows Sec. 5.1; ties
+ * Sec. 5.2 around Eq. (18)).  For every row, among scores[b,i,0:n_p] choose
+ * the m_p largest; equal scores go to the lower index; NaN ranks below every
+ * number; -0.0 equals +0.0.
+ *
+ *   scores [B, T, ld] f32 (only s < n_p is read), ld >= n_kv
+ *   idx    [B, T, topk] int32 out: the chosen s in ascending order, then -1
+ *          up to topk entries.
+ * Supports n_kv <= 262144.
+ */
+int dsa_topk(const dsa_dims* dims, const float* scores, int64_t ld, int32_t* idx, void* stream);
+
+/*
+ * Sparse MLA attention in MQA mode (Eq. (2), Sec. 1.1; renormalised softmax
+ * over the selected set, Eq. (19), Sec. 5.2).  For every head h of row i:
+ *   z_s   = sm_scale * sum_{d<Dk} q[b,i,h,d] * kv[b,s,d]       s in the row's set
+ *   out   = sum_s softmax(z)_s * kv[b,s,0:Dv]
+ *   lse   = max_s z_s + log(sum_s exp(z_s - max_s z_s))
+ * The set of row i is {idx[b,i,j] : j < topk, 0 <= idx[b,i,j] < n_kv};
+ * other entries (e.g. -1 padding) are skipped.  A row with an empty set
+ * gets out = 0 and lse = -inf.
+ *
+ *   q    [B, T, H, Dk]  bf16       kv  [B, S, Dk] bf16
+ *   idx  [B, T, topk]   int32      out [B, T, H, Dv] bf16
+ *   lse  [B, T, H]      f32 or NULL
+ *   ws   workspace of at least dsa_attn_workspace_size(dims) bytes (may be
+ *        NULL when that size is 0).
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; softmax is fp32.
+ */
+size_t dsa_attn_workspace_size(const dsa_dims* dims);
+int dsa_sparse_mla_attn(const dsa_dims* dims, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                        float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * The whole forward path: indexer -> top-k -> sparse MLA, processed in
+ * chunks of query rows so that each chunk's scores stay in a workspace
+ * slice.  Inputs and outputs are those of the three calls above.
+ *   idx_out  [B, T, topk] int32 or NULL: if given, receives the selection.
+ * The result equals, bit for bit, running dsa_indexer_scores, dsa_topk and
+ * dsa_sparse_mla_attn one after the other.
+ * ws must hold dsa_forward_workspace_size(dims) bytes.
+ */
+size_t dsa_forward_workspace_size(const dsa_dims* dims);
+int dsa_forward(const dsa_dims* dims, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
+                const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const uint16_t* kv,
+                float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Status text, thread-local last error message, ABI version (major*100+minor). */
+const char* dsa_status_string(int status);
+const char* dsa_last_error(void);
+int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

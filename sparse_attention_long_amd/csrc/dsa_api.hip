@@ -1,0 +1,314 @@
+// C ABI of the DSA forward path: argument validation, workspace planning and
+// kernel dispatch.  Every check runs on the host before the first HIP call,
+// so invalid calls leave outputs untouched and launch nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return DSA_OK;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+int check_common(const dsa_dims* d) {
+  REQUIRE(d != nullptr, DSA_ERR_INVALID_ARG, "dims is NULL");
+  REQUIRE(d->batch >= 1 && d->n_q >= 1 && d->n_kv >= 1, DSA_ERR_INVALID_ARG,
+          "batch, n_q and n_kv must be >= 1 (got %d, %d, %d)", d->batch, d->n_q, d->n_kv);
+  REQUIRE(d->q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0 (got %d)", d->q_pos0);
+  REQUIRE((int64_t)d->q_pos0 + d->n_q <= d->n_kv, DSA_ERR_INVALID_ARG,
+          "query positions q_pos0 + n_q (%lld) exceed n_kv (%d)", (long long)d->q_pos0 + d->n_q, d->n_kv);
+  REQUIRE(d->topk >= 1 && d->topk <= 2048, DSA_ERR_UNSUPPORTED, "topk must be in [1, 2048] (got %d)", d->topk);
+  REQUIRE((int64_t)d->batch * d->n_q <= (1ll << 30), DSA_ERR_UNSUPPORTED, "batch * n_q too large");
+  return DSA_OK;
+}
+
+int check_indexer_dims(const dsa_dims* d) {
+  REQUIRE(d->idx_heads >= 1 && d->idx_heads <= 64, DSA_ERR_UNSUPPORTED,
+          "idx_heads must be in [1, 64] (got %d)", d->idx_heads);
+  REQUIRE(d->idx_dim >= 16 && d->idx_dim <= 128 && d->idx_dim % 16 == 0, DSA_ERR_UNSUPPORTED,
+          "idx_dim must be a multiple of 16 in [16, 128] (got %d)", d->idx_dim);
+  return DSA_OK;
+}
+
+int check_attn_dims(const dsa_dims* d) {
+  REQUIRE(d->heads >= 1 && d->dim_qk >= 1 && d->dim_v >= 1 && d->dim_v <= d->dim_qk, DSA_ERR_INVALID_ARG,
+          "heads/dim_qk/dim_v inconsistent (%d, %d, %d)", d->heads, d->dim_qk, d->dim_v);
+  REQUIRE(dsa::attn_dims_supported(d->heads, d->dim_qk, d->dim_v), DSA_ERR_UNSUPPORTED,
+          "attention dims (heads %d, dim_qk %d, dim_v %d) not built; supported: dim_qk 576 / dim_v 512 "
+          "with heads <= 128, dim_qk 80 / dim_v 64 with heads <= 32",
+          d->heads, d->dim_qk, d->dim_v);
+  return DSA_OK;
+}
+
+// Split of the selected slots across workgroups for attention: enough
+// workgroups to cover the 256 compute units, at least 128 slots per split.
+int attn_nsplit(const dsa_dims* d) {
+  const int64_t rows = (int64_t)d->batch * d->n_q;
+  if (rows >= 256) return 1;
+  int ns = (int)((256 + rows - 1) / rows);
+  const int max_ns = (d->topk + 127) / 128;
+  if (ns > max_ns) ns = max_ns;
+  if (ns > 16) ns = 16;
+  return ns < 1 ? 1 : ns;
+}
+
+size_t attn_partial_bytes(const dsa_dims* d, int64_t rows_per_seq) {
+  const int ns = attn_nsplit(d);
+  if (ns <= 1) return 0;
+  return (size_t)d->batch * rows_per_seq * ns * d->heads * ((size_t)d->dim_v + 1) * sizeof(float);
+}
+
+// Query rows per chunk of dsa_forward: keep a chunk's scores near 128 MB.
+int64_t forward_chunk_rows(const dsa_dims* d) {
+  const int64_t budget = 128ll << 20;
+  int64_t tc = budget / ((int64_t)d->batch * d->n_kv * 4);
+  if (tc >= 64) tc = tc / 32 * 32;
+  if (tc < 1) tc = 1;
+  if (tc > d->n_q) tc = d->n_q;
+  return tc;
+}
+
+struct ForwardLayout {
+  int64_t tc;
+  size_t scores_off, idx_off, part_off, total;
+};
+
+ForwardLayout forward_layout(const dsa_dims* d) {
+  ForwardLayout L;
+  L.tc = forward_chunk_rows(d);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  L.scores_off = 0;
+  L.idx_off = up((size_t)d->batch * L.tc * d->n_kv * sizeof(float));
+  L.part_off = L.idx_off + up((size_t)d->batch * L.tc * d->topk * sizeof(int32_t));
+  L.total = L.part_off + up(attn_partial_bytes(d, L.tc));
+  return L;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w,
+                              const uint8_t* k_idx, const float* k_scale, float* scores, int64_t ld,
+                              int64_t i0, int rows, int64_t sc_rows_b) {
+  dsa::IndexerArgs a;
+  a.q_idx = q_idx + i0 * d->idx_heads * d->idx_dim;
+  a.q_scale = q_scale + i0;
+  a.w = w + i0 * d->idx_heads;
+  a.k_idx = k_idx;
+  a.k_scale = k_scale;
+  a.scores = scores;
+  a.ld = ld;
+  a.qrows_b = d->n_q;
+  a.sc_rows_b = sc_rows_b;
+  a.B = d->batch;
+  a.rows = rows;
+  a.pos0 = d->q_pos0 + (int)i0;
+  a.S = d->n_kv;
+  a.HI = d->idx_heads;
+  a.dI = d->idx_dim;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return 100; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported dimensions";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+int dsa_indexer_scores(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
+                       const uint8_t* k_idx, const float* k_scale, float* scores, int64_t ld, void* stream) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  if ((st = check_indexer_dims(d)) != DSA_OK) return st;
+  REQUIRE(q_idx && q_scale && w_idx && k_idx && k_scale && scores, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16), DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+  REQUIRE(aligned(q_scale, 4) && aligned(k_scale, 4) && aligned(scores, 4) && aligned(w_idx, 2),
+          DSA_ERR_INVALID_ARG, "misaligned scale/score/weight pointer");
+  REQUIRE(ld >= d->n_kv, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= n_kv (%d)", (long long)ld, d->n_kv);
+  const dsa::IndexerArgs a =
+      indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld, 0, d->n_q, d->n_q);
+  return hip_status(dsa::launch_indexer(a, d->n_q <= dsa::kIndexerDecodeMaxRows, (hipStream_t)stream),
+                    "indexer launch");
+}
+
+int dsa_topk(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, void* stream) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  REQUIRE(scores && idx, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(scores, 4) && aligned(idx, 4), DSA_ERR_INVALID_ARG, "misaligned scores/idx pointer");
+  REQUIRE(ld >= d->n_kv, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= n_kv (%d)", (long long)ld, d->n_kv);
+  REQUIRE(d->n_kv <= dsa::topk_max_kv(), DSA_ERR_UNSUPPORTED, "n_kv (%d) exceeds the top-k limit %d", d->n_kv,
+          dsa::topk_max_kv());
+  dsa::TopkArgs a;
+  a.scores = scores;
+  a.idx = idx;
+  a.ld = ld;
+  a.sc_rows_b = d->n_q;
+  a.idx_rows_b = d->n_q;
+  a.B = d->batch;
+  a.rows = d->n_q;
+  a.pos0 = d->q_pos0;
+  a.S = d->n_kv;
+  a.k = d->topk;
+  return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "top-k launch");
+}
+
+size_t dsa_attn_workspace_size(const dsa_dims* d) {
+  if (check_common(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
+  return attn_partial_bytes(d, d->n_q);
+}
+
+static int validate_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                         float sm_scale, const uint16_t* out, const float* lse, bool idx_required) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  if ((st = check_attn_dims(d)) != DSA_OK) return st;
+  REQUIRE(q && kv && out && (idx || !idx_required), DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16) && aligned(idx, 4) && aligned(lse, 4),
+          DSA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned; idx and lse 4-byte aligned");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  return DSA_OK;
+}
+
+int dsa_sparse_mla_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                        float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = validate_attn(d, q, kv, idx, sm_scale, out, lse, true)) != DSA_OK) return st;
+  const size_t need = attn_partial_bytes(d, d->n_q);
+  REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), DSA_ERR_WORKSPACE,
+          "attention needs %zu workspace bytes (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  REQUIRE(need == 0 || aligned(ws, 16), DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  dsa::AttnArgs a;
+  a.q = q;
+  a.kv = kv;
+  a.idx = idx;
+  a.out = out;
+  a.lse = lse;
+  a.nsplit = attn_nsplit(d);
+  const size_t rows_total = (size_t)d->batch * d->n_q;
+  a.part_o = (float*)ws;
+  a.part_lse = a.nsplit > 1 ? (float*)ws + rows_total * a.nsplit * d->heads * d->dim_v : nullptr;
+  a.qrows_b = d->n_q;
+  a.idx_rows_b = d->n_q;
+  a.B = d->batch;
+  a.rows = d->n_q;
+  a.S = d->n_kv;
+  a.H = d->heads;
+  a.Dk = d->dim_qk;
+  a.Dv = d->dim_v;
+  a.k = d->topk;
+  a.sm_scale = sm_scale;
+  return hip_status(dsa::launch_sparse_mla(a, (hipStream_t)stream), "attention launch");
+}
+
+size_t dsa_forward_workspace_size(const dsa_dims* d) {
+  if (check_common(d) != DSA_OK || check_indexer_dims(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
+  return forward_layout(d).total;
+}
+
+int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
+                const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const uint16_t* kv, float sm_scale,
+                uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = validate_attn(d, q, kv, idx_out, sm_scale, out, lse, false)) != DSA_OK) return st;
+  if ((st = check_indexer_dims(d)) != DSA_OK) return st;
+  REQUIRE(q_idx && q_scale && w_idx && k_idx && k_scale, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16), DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+  REQUIRE(aligned(q_scale, 4) && aligned(k_scale, 4) && aligned(w_idx, 2), DSA_ERR_INVALID_ARG,
+          "misaligned scale/weight pointer");
+  REQUIRE(d->n_kv <= dsa::topk_max_kv(), DSA_ERR_UNSUPPORTED, "n_kv (%d) exceeds the top-k limit %d", d->n_kv,
+          dsa::topk_max_kv());
+  const ForwardLayout L = forward_layout(d);
+  REQUIRE(ws != nullptr && ws_bytes >= L.total, DSA_ERR_WORKSPACE, "forward needs %zu workspace bytes (got %zu)",
+          L.total, ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  float* sc = (float*)(wsb + L.scores_off);
+  const bool decode_form = d->n_q <= dsa::kIndexerDecodeMaxRows;
+  const int nsplit = attn_nsplit(d);
+  for (int64_t i0 = 0; i0 < d->n_q; i0 += L.tc) {
+    const int rows = (int)((d->n_q - i0) < L.tc ? (d->n_q - i0) : L.tc);
+    const dsa::IndexerArgs ia = indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, sc, d->n_kv, i0, rows, L.tc);
+    hipError_t e = dsa::launch_indexer(ia, decode_form, s);
+    if (e != hipSuccess) return hip_status(e, "indexer launch");
+
+    dsa::TopkArgs ta;
+    ta.scores = sc;
+    ta.ld = d->n_kv;
+    ta.sc_rows_b = L.tc;
+    ta.idx = idx_out ? idx_out + i0 * d->topk : (int32_t*)(wsb + L.idx_off);
+    ta.idx_rows_b = idx_out ? d->n_q : L.tc;
+    ta.B = d->batch;
+    ta.rows = rows;
+    ta.pos0 = d->q_pos0 + (int)i0;
+    ta.S = d->n_kv;
+    ta.k = d->topk;
+    e = dsa::launch_topk(ta, s);
+    if (e != hipSuccess) return hip_status(e, "top-k launch");
+
+    dsa::AttnArgs aa;
+    aa.q = q + i0 * d->heads * d->dim_qk;
+    aa.kv = kv;
+    aa.idx = ta.idx;
+    aa.idx_rows_b = ta.idx_rows_b;
+    aa.out = out + i0 * d->heads * d->dim_v;
+    aa.lse = lse ? lse + i0 * d->heads : nullptr;
+    aa.nsplit = nsplit;
+    aa.part_o = (float*)(wsb + L.part_off);
+    aa.part_lse = nsplit > 1 ? aa.part_o + (size_t)d->batch * rows * nsplit * d->heads * d->dim_v : nullptr;
+    aa.qrows_b = d->n_q;
+    aa.B = d->batch;
+    aa.rows = rows;
+    aa.S = d->n_kv;
+    aa.H = d->heads;
+    aa.Dk = d->dim_qk;
+    aa.Dv = d->dim_v;
+    aa.k = d->topk;
+    aa.sm_scale = sm_scale;
+    e = dsa::launch_sparse_mla(aa, s);
+    if (e != hipSuccess) return hip_status(e, "attention launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

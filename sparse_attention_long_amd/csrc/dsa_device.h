@@ -1,0 +1,78 @@
+// Device-side helpers shared by the DSA kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// 16x16x128 FP8(E4M3) x FP8(E4M3) -> fp32 MFMA with unit block scales
+// (E8M0 127 = 2^0).  Operand layout (verified on gfx950): lane l holds row
+// (A) / column (B) l%16 and K bytes [32*(l/16), 32*(l/16)+32); the result
+// lane l holds rows 4*(l/16)+r, r=0..3, of column l%16.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// 32x32x16 bf16 MFMA.  Lane l holds row (A) / column (B) l%32 and K elements
+// [8*(l/32), 8*(l/32)+8); the result element j of lane l is row
+// 8*(j/4) + 4*(l/32) + j%4 of column l%32.
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Exchange across wave halves.  For lanes l < 32 the result is
+// x[l] + x[l+32]; for lanes l >= 32 it is y[l-32] + y[l].
+__device__ __forceinline__ float reduce_halves(float x, float y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Same across 16-lane rows: lanes in rows 0 and 2 get x[l] + x[l+16];
+// lanes in rows 1 and 3 get y[l-16] + y[l].
+__device__ __forceinline__ float reduce_rows16(float x, float y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reduce-scatter of four per-lane partials over the four 16-lane rows of a
+// wave: afterwards lane l (row g = l/16, column n = l%16) holds
+// sum_{g'} p[g][g'*16 + n].  The addition tree is fixed, so every caller
+// gets bit-identical sums for the same partials.
+__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
+  const float a = reduce_halves(p0, p2);   // rows 0,1: p0 sums; rows 2,3: p2 sums
+  const float b = reduce_halves(p1, p3);   // rows 0,1: p1 sums; rows 2,3: p3 sums
+  return reduce_rows16(a, b);              // row 0:p0 row 1:p1 row 2:p2 row 3:p3
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace dsa

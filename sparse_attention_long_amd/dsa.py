@@ -1,0 +1,124 @@
+"""Python binding of the DSA C ABI (include/dsa.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensor arguments
+may be torch tensors on the GPU (their data pointers are passed) or plain
+integer device addresses.  `stream` defaults to torch's current stream.
+A non-zero status raises DSAError with the library's own message.  There is
+no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+
+# Every symbol include/dsa.h declares.
+EXPORTS = (
+    "dsa_indexer_scores", "dsa_topk", "dsa_attn_workspace_size", "dsa_sparse_mla_attn",
+    "dsa_forward_workspace_size", "dsa_forward", "dsa_status_string", "dsa_last_error", "dsa_version",
+)
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q", "n_kv", "q_pos0", "idx_heads", "idx_dim", "heads", "dim_qk", "dim_v", "topk")]
+
+    @classmethod
+    def of(cls, wl=None, **kw):
+        """Dims from a workload object (anything with these attribute names) and/or keywords."""
+        vals = {n: getattr(wl, n) for n, _ in cls._fields_} if wl is not None else {}
+        vals.update(kw)
+        return cls(**vals)
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(Dims)
+        L.dsa_indexer_scores.argtypes = [D, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]
+        L.dsa_topk.argtypes = [D, _P, ctypes.c_int64, _P, _P]
+        L.dsa_attn_workspace_size.argtypes = [D]
+        L.dsa_attn_workspace_size.restype = ctypes.c_size_t
+        L.dsa_sparse_mla_attn.argtypes = [D, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dsa_forward_workspace_size.argtypes = [D]
+        L.dsa_forward_workspace_size.restype = ctypes.c_size_t
+        L.dsa_forward.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dsa_status_string.argtypes = [ctypes.c_int]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_last_error.restype = ctypes.c_char_p
+        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int):
+    if status != OK:
+        L = lib()
+        raise DSAError(status, f"{L.dsa_status_string(status).decode()}: {L.dsa_last_error().decode()}")
+
+
+def dsa_version() -> int:
+    return lib().dsa_version()
+
+
+def dsa_indexer_scores(dims: Dims, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld: int, stream=None):
+    _check(lib().dsa_indexer_scores(ctypes.byref(dims), _ptr(q_idx), _ptr(q_scale), _ptr(w_idx), _ptr(k_idx),
+                                    _ptr(k_scale), _ptr(scores), int(ld), _stream(stream)))
+
+
+def dsa_topk(dims: Dims, scores, ld: int, idx, stream=None):
+    _check(lib().dsa_topk(ctypes.byref(dims), _ptr(scores), int(ld), _ptr(idx), _stream(stream)))
+
+
+def dsa_attn_workspace_size(dims: Dims) -> int:
+    return int(lib().dsa_attn_workspace_size(ctypes.byref(dims)))
+
+
+def dsa_sparse_mla_attn(dims: Dims, q, kv, idx, sm_scale: float, out, lse=None, ws=None, ws_bytes: int = 0,
+                        stream=None):
+    _check(lib().dsa_sparse_mla_attn(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), float(sm_scale), _ptr(out),
+                                     _ptr(lse), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def dsa_forward_workspace_size(dims: Dims) -> int:
+    return int(lib().dsa_forward_workspace_size(ctypes.byref(dims)))
+
+
+def dsa_forward(dims: Dims, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_scale: float, out, lse=None,
+                idx_out=None, ws=None, ws_bytes: int = 0, stream=None):
+    _check(lib().dsa_forward(ctypes.byref(dims), _ptr(q_idx), _ptr(q_scale), _ptr(w_idx), _ptr(k_idx),
+                             _ptr(k_scale), _ptr(q), _ptr(kv), float(sm_scale), _ptr(out), _ptr(lse),
+                             _ptr(idx_out), _ptr(ws), int(ws_bytes), _stream(stream)))

@@ -1,0 +1,78 @@
+"""Device-side filling of workload inputs (HIP generator library via ctypes,
+torch for device memory).  Produces the same bytes as the host builders in
+``workloads.py``."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import gen
+from .workloads import Workload, _low_rank
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_synth.so")
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.synth_fill_bf16.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        L.synth_fill_f32.argtypes = L.synth_fill_bf16.argtypes
+        L.synth_fill_e4m3_tokens.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.synth_stream_key.argtypes = [ctypes.c_uint64, ctypes.c_int32]
+        L.synth_stream_key.restype = ctypes.c_uint64
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise RuntimeError(f"synth device fill failed: hipError {rc}")
+
+
+def _stream(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def fill_inputs(wl: Workload, device="cuda"):
+    """Allocate and fill all inputs of `wl` on the device.  Returns a dict of
+    torch tensors: q_idx uint8 [B,T,HI,dI], q_scale f32 [B,T], w_idx int16
+    (bf16 bits) [B,T,HI], k_idx uint8 [B,S,dI], k_scale f32 [B,S],
+    q int16 [B,T,H,Dk], kv int16 [B,S,Dk]."""
+    import torch
+    L = lib()
+    B, T, S = wl.batch, wl.n_q, wl.n_kv
+    HI, dI, H, Dk = wl.idx_heads, wl.idx_dim, wl.heads, wl.dim_qk
+    st = _stream(torch)
+    t = {
+        "q_idx": torch.empty((B, T, HI, dI), dtype=torch.uint8, device=device),
+        "q_scale": torch.empty((B, T), dtype=torch.float32, device=device),
+        "w_idx": torch.empty((B, T, HI), dtype=torch.int16, device=device),
+        "k_idx": torch.empty((B, S, dI), dtype=torch.uint8, device=device),
+        "k_scale": torch.empty((B, S), dtype=torch.float32, device=device),
+        "q": torch.empty((B, T, H, Dk), dtype=torch.int16, device=device),
+        "kv": torch.empty((B, S, Dk), dtype=torch.int16, device=device),
+    }
+    _check(L.synth_fill_e4m3_tokens(wl.seed, gen.TID["q_idx"], 0, B * T, HI * dI,
+                                    t["q_idx"].data_ptr(), t["q_scale"].data_ptr(), st))
+    _check(L.synth_fill_bf16(wl.seed, gen.TID["w_idx"], 0, B * T * HI, wl.w_exp2, t["w_idx"].data_ptr(), st))
+    _check(L.synth_fill_bf16(wl.seed, gen.TID["q"], 0, B * T * H * Dk, 0, t["q"].data_ptr(), st))
+    if wl.low_rank:
+        c, k = _low_rank(wl)
+        codes, scales = gen.quantize_tokens_e4m3(k)
+        t["k_idx"].copy_(torch.from_numpy(codes).reshape(B, S, dI))
+        t["k_scale"].copy_(torch.from_numpy(scales).reshape(B, S))
+        t["kv"].copy_(torch.from_numpy(gen.f32_to_bf16_bits(c).view(np.int16)).reshape(B, S, Dk))
+    else:
+        _check(L.synth_fill_e4m3_tokens(wl.seed, gen.TID["k_idx"], 0, B * S, dI,
+                                        t["k_idx"].data_ptr(), t["k_scale"].data_ptr(), st))
+        _check(L.synth_fill_bf16(wl.seed, gen.TID["kv"], 0, B * S * Dk, 0, t["kv"].data_ptr(), st))
+    return t

@@ -1,0 +1,104 @@
+"""The C ABI library loads without a GPU, exports every symbol include/dsa.h
+declares, and rejects invalid calls on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_long_amd as dsa
+from sparse_attention_long_amd.dsa import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = dsa.lib()
+    declared = _header_functions()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(dsa.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert dsa.dsa_version() == 100
+    L = dsa.lib()
+    assert L.dsa_status_string(0) == b"ok"
+    assert L.dsa_status_string(3) == b"workspace too small"
+
+
+def _dims(**kw):
+    base = dict(batch=1, n_q=8, n_kv=8, q_pos0=0, idx_heads=64, idx_dim=128, heads=128, dim_qk=576, dim_v=512, topk=4)
+    base.update(kw)
+    return Dims(**base)
+
+
+FAKE = 1 << 20   # an aligned, never-dereferenced address: validation fails before any use
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q=0), dsa.dsa.ERR_INVALID_ARG),
+    (dict(q_pos0=-1), dsa.dsa.ERR_INVALID_ARG),
+    (dict(q_pos0=1), dsa.dsa.ERR_INVALID_ARG),           # positions beyond the cache
+    (dict(topk=0), dsa.dsa.ERR_UNSUPPORTED),
+    (dict(topk=2049), dsa.dsa.ERR_UNSUPPORTED),
+    (dict(idx_heads=65), dsa.dsa.ERR_UNSUPPORTED),
+    (dict(idx_dim=100), dsa.dsa.ERR_UNSUPPORTED),
+])
+def test_indexer_validation(kw, status):
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_indexer_scores(_dims(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, stream=0)
+    assert e.value.status == status
+
+
+def test_indexer_rejects_small_ld_null_and_misaligned():
+    for args, ld in (((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 7), ((FAKE, FAKE, FAKE, 0, FAKE, FAKE), 8),
+                     ((FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE), 8)):
+        with pytest.raises(dsa.DSAError) as e:
+            dsa.dsa_indexer_scores(_dims(), *args, ld, stream=0)
+        assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+
+
+def test_topk_validation():
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_topk(_dims(n_kv=300000, n_q=1, q_pos0=0), FAKE, 300000, FAKE, stream=0)
+    assert e.value.status == dsa.dsa.ERR_UNSUPPORTED
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_topk(_dims(), FAKE, 4, FAKE, stream=0)
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+
+
+def test_attention_validation_and_workspace():
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_sparse_mla_attn(_dims(dim_qk=128, dim_v=64), FAKE, FAKE, FAKE, 0.1, FAKE, stream=0)
+    assert e.value.status == dsa.dsa.ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(dsa.DSAError) as e:
+            dsa.dsa_sparse_mla_attn(_dims(), FAKE, FAKE, FAKE, bad, FAKE, stream=0)
+        assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+    # decode-like shapes split the selected set and need a workspace
+    d = _dims(batch=64, n_q=1, n_kv=131072, q_pos0=131071, topk=2048)
+    need = dsa.dsa_attn_workspace_size(d)
+    assert need == 64 * 4 * 128 * 513 * 4
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_sparse_mla_attn(d, FAKE, FAKE, FAKE, 0.1, FAKE, ws=FAKE, ws_bytes=need - 1, stream=0)
+    assert e.value.status == dsa.dsa.ERR_WORKSPACE
+    # many rows: no split, no workspace
+    assert dsa.dsa_attn_workspace_size(_dims(n_q=4096, n_kv=4096, topk=2048)) == 0
+
+
+def test_forward_workspace_plan():
+    d = _dims(n_q=131072, n_kv=131072, topk=2048)
+    ws = dsa.dsa_forward_workspace_size(d)
+    # 256-row chunks: 128 MiB of scores plus 2 MiB of indices
+    assert ws == 256 * 131072 * 4 + 256 * 2048 * 4
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_forward(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE, ws=FAKE, ws_bytes=ws - 1, stream=0)
+    assert e.value.status == dsa.dsa.ERR_WORKSPACE
+    assert dsa.dsa_forward_workspace_size(_dims(heads=7, dim_qk=100)) == 0   # unsupported dims

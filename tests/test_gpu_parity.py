@@ -1,0 +1,356 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Small workloads are compared everywhere; the full-size
+workloads run in the configuration the benchmark times and are compared on
+sampled rows that the oracle computes one by one."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_long_amd as dsa
+from oracle import dsa_oracle as O
+from synth import workloads as W
+from synth import device as SD
+
+from dsa_parity import (ATTN_MAX_REL, LSE_ABS, SCORE_REL_RMS, HostSide, attn_errors, bf16_tensor_to_f64,
+                        check_selection, score_rel_rms, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.lib()   # raises if the HIP library is missing: no fallback path exists
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def host_dev_inputs(wl):
+    h = W.host_inputs(wl)
+    return h, {k: to_dev(v) for k, v in h.items()}
+
+
+def run_indexer(wl, d, ld=None, sentinel=float("nan")):
+    ld = ld or wl.n_kv
+    sc = torch.full((wl.batch, wl.n_q, ld), sentinel, dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores(dsa.Dims.of(wl), d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], sc, ld)
+    torch.cuda.synchronize()
+    return sc
+
+
+def sample_rows(T, extra=()):
+    rows = {0, 1, 15, 16, 31, 32, 33, 63, 64, T // 2, T - 33, T - 32, T - 17, T - 2, T - 1, *extra}
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+# ----------------------------------------------------------------- generator
+def test_device_generator_matches_host():
+    tiny = W.WORKLOADS["tiny"]
+    h = W.host_inputs(tiny)
+    d = SD.fill_inputs(tiny)
+    torch.cuda.synchronize()
+    for k, v in h.items():
+        got = d[k].cpu().numpy()
+        assert np.array_equal(got.view(v.dtype) if v.dtype == np.uint16 else got, v), k
+    wl = W.WORKLOADS["p4k"]
+    d = SD.fill_inputs(wl)
+    torch.cuda.synchronize()
+    rows = [0, 1, 1234, 4095]
+    c, s = W.q_idx_fp8(wl, 0, rows)
+    assert np.array_equal(d["q_idx"][0, rows].cpu().numpy(), c)
+    assert np.array_equal(d["q_scale"][0, rows].cpu().numpy(), s)
+    assert np.array_equal(d["q"][0, rows].cpu().numpy().view(np.uint16), W.q_bf16(wl, 0, rows))
+    assert np.array_equal(d["w_idx"][0].cpu().numpy().view(np.uint16), W.w_idx_bf16(wl, 0, range(4096)))
+    c, s = W.k_idx_fp8(wl, 0, 0, 4096)
+    assert np.array_equal(d["k_idx"][0].cpu().numpy(), c) and np.array_equal(d["k_scale"][0].cpu().numpy(), s)
+    assert np.array_equal(d["kv"][0, rows].cpu().numpy().view(np.uint16), W.kv_bf16_rows(wl, 0, rows))
+
+
+# ----------------------------------------------------------------- indexer
+def test_indexer_tiny_all_rows():
+    wl = W.WORKLOADS["tiny"]
+    h, d = host_dev_inputs(wl)
+    sc = run_indexer(wl, d).cpu().numpy()
+    hs = HostSide(wl)
+    pairs = []
+    for i in range(wl.n_q):
+        n = min(i + 1, wl.n_kv)
+        ref = hs.scores(i)
+        pairs.append((sc[0, i, :n], ref))
+        assert np.all(np.isnan(sc[0, i, n:])), f"row {i}: wrote beyond the causal window"
+    err = score_rel_rms(pairs)
+    _say("tiny indexer rel RMS", err)
+    assert err <= SCORE_REL_RMS
+
+
+INDEXER_CASES = {
+    "p4k": W.WORKLOADS["p4k"],
+    "ragged_3001": W.custom("p4k", n_q=3001, n_kv=3001),
+    "chunk_pos0": W.custom("p4k", n_q=700, n_kv=3095, q_pos0=2395),
+    "rows5": W.custom("p4k", n_q=5, n_kv=1037, q_pos0=1032),
+    "decode_b3": W.custom("dec64", batch=3, n_kv=5003, q_pos0=5002),
+    "decode_t3": W.custom("dec64", batch=2, n_q=3, n_kv=4099, q_pos0=4096),
+    "two_chunks": W.custom("p4k", n_q=1024, n_kv=65536, q_pos0=64512),
+}
+
+
+@pytest.mark.parametrize("name", list(INDEXER_CASES))
+def test_indexer_production_dims(name):
+    wl = INDEXER_CASES[name]
+    d = SD.fill_inputs(wl)
+    ld = wl.n_kv + 7
+    sc = run_indexer(wl, d, ld=ld)
+    pairs = []
+    for b in sorted({0, wl.batch - 1}):
+        hs = HostSide(wl, b)
+        for i in sample_rows(wl.n_q):
+            n = min(wl.q_pos0 + i + 1, wl.n_kv)
+            row = sc[b, i].cpu().numpy()
+            assert not np.any(np.isnan(row[:n])), (b, i)
+            assert np.all(np.isnan(row[n:])), (b, i)
+            pairs.append((row[:n], hs.scores(i)))
+    err = score_rel_rms(pairs)
+    _say(name, "indexer rel RMS", err)
+    assert err <= SCORE_REL_RMS
+
+
+# ----------------------------------------------------------------- top-k
+def run_topk(scores_np, k, pos0=None):
+    B, T, S = scores_np.shape
+    pos0 = S - T if pos0 is None else pos0
+    dims = dsa.Dims(batch=B, n_q=T, n_kv=S, q_pos0=pos0, idx_heads=64, idx_dim=128, heads=128, dim_qk=576,
+                    dim_v=512, topk=k)
+    idx = torch.full((B, T, k), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(dims, to_dev(scores_np.astype(np.float32)), S, idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def assert_topk_exact(scores_np, k, pos0=None):
+    B, T, S = scores_np.shape
+    pos0 = S - T if pos0 is None else pos0
+    got = run_topk(scores_np, k, pos0)
+    for b in range(B):
+        for i in range(T):
+            n = min(pos0 + i + 1, S)
+            want = O.topk_row(scores_np[b, i, :n], k)
+            assert np.array_equal(got[b, i], want), (b, i, n)
+
+
+def test_topk_exact_on_oracle_scores_tiny():
+    wl = W.WORKLOADS["tiny"]
+    hs = HostSide(wl)
+    sc = np.full((1, wl.n_q, wl.n_kv), np.nan, np.float32)
+    for i in range(wl.n_q):
+        sc[0, i, :i + 1] = hs.scores(i)
+    assert_topk_exact(sc, wl.topk, 0)
+
+
+def test_topk_exact_on_oracle_scores_production():
+    wl = W.custom("p4k", n_q=96, n_kv=6000, q_pos0=5904)
+    hs = HostSide(wl)
+    sc = np.full((1, wl.n_q, wl.n_kv), np.nan, np.float32)
+    for i in range(wl.n_q):
+        sc[0, i, :wl.q_pos0 + i + 1] = hs.scores(i)
+    assert_topk_exact(sc, 2048)
+
+
+@pytest.mark.parametrize("case", ["ties_small_ints", "nan_and_zeros", "all_equal", "wide_bin", "k_plus_one",
+                                  "negative", "k1", "long_rows"])
+def test_topk_exact_adversarial(case):
+    rs = np.random.RandomState(zlib.crc32(case.encode()))
+    if case == "ties_small_ints":
+        sc, k = np.round(rs.randn(2, 40, 5000) * 2).astype(np.float32), 300
+    elif case == "nan_and_zeros":
+        sc = rs.randn(1, 20, 3000).astype(np.float32)
+        sc[rs.rand(*sc.shape) < 0.3] = np.nan
+        sc[rs.rand(*sc.shape) < 0.3] = 0.0
+        sc[rs.rand(*sc.shape) < 0.3] = -0.0
+        k = 2048
+    elif case == "all_equal":
+        sc, k = np.full((1, 8, 9000), 1.5, np.float32), 2048
+    elif case == "wide_bin":   # one top-11-bit bin holds > 4096 keys: multi-pass path
+        sc = (1.0 + rs.rand(1, 6, 30000) * 0.2).astype(np.float32)
+        sc[0, :, ::7] = 1.1          # exact ties inside the wide bin
+        k = 2048
+    elif case == "k_plus_one":
+        sc, k = rs.randn(1, 3, 2049).astype(np.float32), 2048
+    elif case == "negative":
+        sc, k = (-np.abs(rs.randn(1, 10, 4000)) * 1e-30).astype(np.float32), 1000
+    elif case == "k1":
+        sc, k = rs.randn(3, 5, 777).astype(np.float32), 1
+    else:
+        sc, k = rs.randn(1, 4, 131072).astype(np.float32), 2048
+    assert_topk_exact(sc, k)
+
+
+# ----------------------------------------------------------------- attention
+def run_attn(wl, q_dev, kv_dev, idx_np, rows):
+    dims = dsa.Dims.of(wl, n_q=rows, q_pos0=0)
+    B = wl.batch
+    out = torch.zeros((B, rows, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
+    lse = torch.zeros((B, rows, wl.heads), dtype=torch.float32, device="cuda")
+    nws = dsa.dsa_attn_workspace_size(dims)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_attn(dims, q_dev, kv_dev, to_dev(idx_np.astype(np.int32)), wl.sm_scale, out, lse, ws, nws)
+    torch.cuda.synchronize()
+    return bf16_tensor_to_f64(out), lse.cpu().numpy(), nws
+
+
+def _attn_case(wl, rows, sel_of_row, q_mul=1.0):
+    """Attention only: q rows chosen by `rows` (positions 0.. of a [1, len(rows)] call)."""
+    B = wl.batch
+    hs = [HostSide(wl, b) for b in range(B)]
+    q = np.stack([np.stack([W.q_bf16(wl, b, [i])[0] for i in rows]) for b in range(B)])
+    if q_mul != 1.0:
+        from synth import gen
+        q = np.stack([gen.f32_to_bf16_bits(O.bf16_decode(q[b]).astype(np.float32) * np.float32(q_mul)) for b in range(B)])
+    idx = np.stack([np.stack([sel_of_row(b, i) for i in rows]) for b in range(B)])
+    kv = np.stack([W.kv_bf16_rows(wl, b, np.arange(wl.n_kv)) for b in range(B)])
+    o, lse, nws = run_attn(wl, to_dev(q), to_dev(kv), idx, len(rows))
+    worst, worst_lse = 0.0, 0.0
+    for b in range(B):
+        for n, i in enumerate(rows):
+            qv = O.bf16_decode(q[b, n])
+            kvf = O.bf16_decode(kv[b])
+            ref_o, ref_lse = O.sparse_mla_row(qv, kvf, idx[b, n], wl.sm_scale, wl.dim_v)
+            if not np.any(idx[b, n] >= 0):
+                assert np.all(o[b, n] == 0) and np.all(np.isneginf(lse[b, n]))
+                continue
+            worst = max(worst, attn_errors(o[b, n], ref_o).max())
+            worst_lse = max(worst_lse, np.abs(lse[b, n] - ref_lse).max())
+    return worst, worst_lse, nws
+
+
+def test_attention_tiny_oracle_selection():
+    wl = W.WORKLOADS["tiny"]
+    hs = HostSide(wl)
+    worst, wl_lse, _ = _attn_case(wl, list(range(wl.n_q)), lambda b, i: O.topk_row(hs.scores(i), wl.topk))
+    _say("tiny attention max rel err", worst, "lse abs err", wl_lse)
+    assert worst <= ATTN_MAX_REL and wl_lse <= LSE_ABS
+
+
+def test_attention_production_dims_rows():
+    wl = W.custom("p4k", n_kv=4096)
+    hs = HostSide(wl)
+    rows = [0, 1, 31, 32, 100, 2046, 2047, 2048, 3000, 4095]
+    worst, wlse, nws = _attn_case(wl, rows, lambda b, i: O.topk_row(hs.scores(i), wl.topk))
+    _say("p4k rows attention max rel err", worst, "lse", wlse, "ws", nws)
+    assert worst <= ATTN_MAX_REL and wlse <= LSE_ABS
+
+
+def test_attention_split_path_and_padding():
+    # few rows -> the selected set is split across workgroups and merged
+    wl = W.custom("dec64", batch=4, n_kv=9000, q_pos0=8999)
+    rs = np.random.RandomState(3)
+
+    def sel(b, i):
+        m = [2048, 1500, 37, 0][b]
+        out = np.full(2048, -1, np.int32)
+        out[:m] = np.sort(rs.choice(9000, size=m, replace=False))
+        return out
+
+    worst, wlse, nws = _attn_case(wl, [0], sel)
+    _say("split attention max rel err", worst, "lse", wlse, "ws", nws)
+    assert nws > 0
+    assert worst <= ATTN_MAX_REL and wlse <= LSE_ABS
+
+
+def test_attention_large_logits_recompute_path():
+    # logits far above the first chunk's maximum force the second pass
+    wl = W.custom("p4k", n_kv=4096)
+    rs = np.random.RandomState(4)
+    worst, wlse, _ = _attn_case(wl, [5, 6, 7], lambda b, i: np.sort(rs.choice(4096, 2048, replace=False)).astype(np.int32),
+                                q_mul=40.0)
+    _say("large-logit attention max rel err", worst, "lse", wlse)
+    assert worst <= ATTN_MAX_REL and wlse <= LSE_ABS * 40
+
+
+# ----------------------------------------------------------------- fused forward
+def run_forward(wl, d, with_idx=True):
+    dims = dsa.Dims.of(wl)
+    out = torch.empty((wl.batch, wl.n_q, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.batch, wl.n_q, wl.heads), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device="cuda") if with_idx else None
+    nws = dsa.dsa_forward_workspace_size(dims)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    dsa.dsa_forward(dims, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], d["q"], d["kv"],
+                    wl.sm_scale, out, lse, idx, ws, nws)
+    torch.cuda.synchronize()
+    return out, lse, idx
+
+
+@pytest.mark.parametrize("name", ["tiny", "p4k", "decode_b3", "chunk_pos0", "two_chunks"])
+def test_forward_bitwise_equals_chained_calls(name):
+    wl = W.WORKLOADS.get(name) or INDEXER_CASES[name]
+    d = SD.fill_inputs(wl)
+    out, lse, idx = run_forward(wl, d)
+    out2, lse2, _ = run_forward(wl, d, with_idx=False)
+    dims = dsa.Dims.of(wl)
+    sc = run_indexer(wl, d)
+    idx_c = torch.empty_like(idx)
+    dsa.dsa_topk(dims, sc, wl.n_kv, idx_c)
+    out_c = torch.empty_like(out)
+    lse_c = torch.empty_like(lse)
+    nws = dsa.dsa_attn_workspace_size(dims)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_attn(dims, d["q"], d["kv"], idx_c, wl.sm_scale, out_c, lse_c, ws, nws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_c)
+    assert torch.equal(out, out_c) and torch.equal(out, out2)
+    assert torch.equal(lse.view(torch.int32), lse_c.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+def check_forward_rows(wl, out, lse, idx, rows_by_seq):
+    worst, worst_lse, recall, amb = 0.0, 0.0, [], 0
+    for b, rows in rows_by_seq.items():
+        hs = HostSide(wl, b)
+        for i in rows:
+            ref_sc = hs.scores(i)
+            gsel = idx[b, i].cpu().numpy()
+            r, a = check_selection(gsel, ref_sc, wl.topk)
+            recall.append(r); amb += a
+            ref_sel = O.topk_row(ref_sc, wl.topk)
+            if not np.array_equal(gsel, ref_sel):
+                continue   # a tie-band swap: outputs legitimately differ
+            ref_o, ref_lse = hs.attention(i, ref_sel)
+            o = bf16_tensor_to_f64(out[b, i])
+            worst = max(worst, attn_errors(o, ref_o).max())
+            worst_lse = max(worst_lse, np.abs(lse[b, i].cpu().numpy() - ref_lse).max())
+    return worst, worst_lse, float(np.mean(recall)), amb
+
+
+def test_forward_tiny_end_to_end():
+    wl = W.WORKLOADS["tiny"]
+    out, lse, idx = run_forward(wl, SD.fill_inputs(wl))
+    worst, wlse, rec, amb = check_forward_rows(wl, out, lse, idx, {0: range(wl.n_q)})
+    _say("tiny forward: attn err", worst, "lse", wlse, "recall", rec, "ambiguous", amb)
+    assert worst <= ATTN_MAX_REL and wlse <= LSE_ABS
+
+
+# ----------------------------------------------------------------- full size (sampled rows)
+FULL = ["p4k", "p32k", "p128k", "dec64"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled(name):
+    wl = W.WORKLOADS[name]
+    d = SD.fill_inputs(wl)
+    out, lse, idx = run_forward(wl, d)
+    del d
+    if wl.n_q == 1:
+        rows = {b: [0] for b in (0, 17, wl.batch - 1)}
+    else:
+        T = wl.n_q
+        rows = {0: sorted({0, 1, 777, 2046, 2047, 2048, 2049, T // 2 + 3, T - 1})}
+    worst, wlse, rec, amb = check_forward_rows(wl, out, lse, idx, rows)
+    _say(name, "forward sampled rows: attn err", worst, "lse", wlse, "recall", rec, "ambiguous", amb)
+    assert worst <= ATTN_MAX_REL and wlse <= LSE_ABS
