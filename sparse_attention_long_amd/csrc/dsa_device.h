@@ -9,6 +9,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -63,6 +64,14 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
   const float a = reduce_halves(p0, p2);   // rows 0,1: p0 sums; rows 2,3: p2 sums
   const float b = reduce_halves(p1, p3);   // rows 0,1: p1 sums; rows 2,3: p3 sums
   return reduce_rows16(a, b);              // row 0:p0 row 1:p1 row 2:p2 row 3:p3
+}
+
+// ds_read_b64_tr_b16 (verified on gfx950): within each 16-lane group, lane
+// c returns element c%4 of the 8-byte chunks addressed by lanes c/4, c/4+4,
+// c/4+8 and c/4+12 of the group.  If lanes 4i..4i+3 address 4 consecutive
+// columns each of row i of a 4 x 16 bf16 block, lane c receives column c.
+__device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4bf*)(p));
 }
 
 __device__ __forceinline__ float max_halves(float x) {

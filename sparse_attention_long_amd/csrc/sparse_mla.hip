@@ -35,48 +35,96 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRefHeadroom = 64.0f;  // log2 units a logit may exceed the reference by
 constexpr int kMaxSlots = 2048;
+constexpr int kLookA = 3;              // QK operand prefetch depth (K steps)
+constexpr int kLookV = 4;              // PV operand prefetch depth (MFMAs)
 
+// LDS tile of one chunk (32 gathered rows), in 16-byte pieces:
+//  part A: the value dims [0, Dv) of every row, row stride RA = PA + padA
+//          pieces, piece p of row r stored at position p ^ ((r / 4) % 4);
+//  part B: the remaining (rope) dims [Dv, Dk), PB pieces per row, piece p of
+//          row r stored at p ^ (r % PB).
+// With RA = 68 (1088 B, 272 dwords = 16 mod 64 banks) both the QK operand
+// reads (16 rows x 16 B per pass) and the PV transposed reads (4 rows x 64 B
+// per pass) touch 64 distinct banks.
 template <int DK, int DV, int NW>
 struct Cfg {
   static constexpr int kKS = DK / 16;            // QK K steps
-  static constexpr int kKSL = kKS / 2;           // K steps whose Q^T operand lives in LDS
-  static constexpr int kKSR = kKS - kKSL;        // K steps whose Q^T operand lives in registers
-  static constexpr int kHeads = NW * 32;
   static constexpr int kNT = DV / 32;            // O^T dim tiles
-  static constexpr int kRS = DK + 8;             // LDS row stride (bf16): +16 B de-aligns banks
-  static constexpr int kPieces = DK / 8;         // 16-byte pieces of data per row
-  static constexpr int kSlotsRow = kRS / 8;      // 16-byte LDS slots per row (last one is padding)
-  static constexpr int kSlots = kChunk * kSlotsRow;
+  static constexpr int kPA = DV / 8;             // pieces of part A per row
+  static constexpr int kPB = (DK - DV) / 8;      // pieces of part B per row
+  static constexpr int kRA = kPA == 64 ? 68 : kPA;   // part A row stride (pieces)
+  static constexpr int kBaseB = kChunk * kRA;    // first piece of part B
+  static constexpr int kTilePieces = kBaseB + kChunk * kPB;
+  static constexpr int kTileElems = kTilePieces * 8;
   static constexpr int kThreads = NW * kWave;
-  static constexpr int kDmaIters = (kSlots + kThreads - 1) / kThreads;
-  static constexpr int kTileElems = kSlots * 8;
-  static constexpr int kQElems = kKSL * 2 * kHeads * 8;   // Q^T part: [ks][half][head][8]
+  // DMA instructions per chunk: one per row of part A when a row is exactly
+  // one wave's 64 pieces, else 64 consecutive pieces each; then part B.
+  static constexpr bool kRowDma = kPA == 64;
+  static constexpr int kDmaA = kRowDma ? kChunk : kChunk * kPA / kWave;
+  static constexpr int kDmaB = kChunk * kPB / kWave;
+  static constexpr int kDma = kDmaA + kDmaB;
+  static_assert(kPA % 4 == 0 && (kChunk * kPA) % kWave == 0 && (kChunk * kPB) % kWave == 0, "tile shape");
+  static_assert((kPB & (kPB - 1)) == 0, "part B width must be a power of two");
+  static_assert(kDma % NW == 0, "DMA instructions must split evenly over waves");
 };
 
-// Gather the 32 rows of chunk c straight into an LDS tile with
-// global_load_lds_dwordx4: each wave instruction fills 64 consecutive
-// 16-byte LDS slots, lane l filling slot base + l from the global row piece
-// that belongs there.  Padding slots are skipped; an invalid row index reads
-// row 0 instead (finite data, masked out of the softmax later).
+__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
+
+// Position (in elements) of logical piece p of row r.
 template <int DK, int DV, int NW>
-__device__ __forceinline__ void gather_dma(uint16_t* tile, const uint16_t* kvb, const int32_t* sidx_c) {
+__device__ __forceinline__ int piece_pos(int r, int p) {
   using C = Cfg<DK, DV, NW>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (p < C::kPA) return (r * C::kRA + (p ^ swz_a(r))) * 8;
+  const int pb = p - C::kPA;
+  return (C::kBaseB + r * C::kPB + (pb ^ (r & (C::kPB - 1)))) * 8;
+}
+
+// Gather one chunk's rows into a tile with global_load_lds_dwordx4: each
+// wave instruction fills 64 consecutive 16-byte LDS pieces, lane l filling
+// piece base + l from the global row piece that belongs there.  Instruction
+// j goes to wave j % NW, so every wave issues kDma / NW instructions.  An
+// invalid row index reads row 0 (finite data, masked out of the softmax).
+// `row_of_lane`: lane j < 32 holds the chunk's j-th row index.
+template <int DK, int DV, int NW>
+__device__ __forceinline__ void gather_dma(uint16_t* tile, const uint16_t* kvb, int row_of_lane) {
+  using C = Cfg<DK, DV, NW>;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));   // recompute the cheap per-lane offsets here, do not hoist them
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int u = 0; u < C::kDmaIters; ++u) {
-    const int base = (u * NW + wave) * kWave;
-    const int q = base + lane;
-    const int r = q / C::kSlotsRow, p = q % C::kSlotsRow;
-    if (q < C::kSlots && p < C::kPieces) {
-      const int s = max(sidx_c[r], 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kvb + (int64_t)s * DK + 8 * p),
-          (__attribute__((address_space(3))) void*)(tile + base * 8), 16, 0, 0);
+  for (int jj = 0; jj < C::kDma / NW; ++jj) {
+    const int j = jj * NW + wave;                 // wave-uniform instruction index
+    // Whether instruction jj of every wave lies in part A or part B is known
+    // at compile time for the shapes built here (no wave straddles).
+    const bool in_a = (jj + 1) * NW <= C::kDmaA ? true : (jj * NW >= C::kDmaA ? false : j < C::kDmaA);
+    const uint16_t* src;
+    uint16_t* dst;
+    if (C::kRowDma && in_a) {
+      // one row per instruction: scalar row base + per-lane swizzled piece
+      const int s = max(__builtin_amdgcn_readlane(row_of_lane, j), 0);
+      const uint16_t* rowp = kvb + (int64_t)s * DK;
+      src = rowp + 8 * (lane ^ swz_a(j));
+      dst = tile + j * C::kRA * 8;
+    } else if (in_a) {
+      const int q = j * kWave + lane;             // piece of the contiguous part A
+      const int r = q / C::kPA, pp = q % C::kPA;
+      const int s = max(__shfl(row_of_lane, r, kWave), 0);
+      src = kvb + (int64_t)s * DK + 8 * (pp ^ swz_a(r));
+      dst = tile + j * kWave * 8;
+    } else {
+      const int q = (j - C::kDmaA) * kWave + lane;  // piece of part B
+      const int r = q / C::kPB, pp = q % C::kPB;
+      const int s = max(__shfl(row_of_lane, r, kWave), 0);
+      src = kvb + (int64_t)s * DK + 8 * (C::kPA + (pp ^ (r & (C::kPB - 1))));
+      dst = tile + (C::kBaseB + (j - C::kDmaA) * kWave) * 8;
     }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 template <int DK, int DV, int NW>
 struct RowState {
@@ -87,35 +135,44 @@ struct RowState {
 };
 
 // One chunk of 32 gathered rows: S^T = C.Q^T, softmax weights against the
-// fixed reference, O^T += V^T.P^T.
+// fixed reference, O^T += V^T.P^T.  `valid` bit r says row r of the chunk
+// holds a selected entry.
 template <int DK, int DV, int NW>
-__device__ __forceinline__ void attend_chunk(const uint16_t* tb, const int32_t* sidx_c, const uint16_t* qlds,
-                                             const v8bf (&qb)[Cfg<DK, DV, NW>::kKSR], float zscale,
-                                             RowState<DK, DV, NW>& rs) {
+__device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid, const v8bf (&qb)[DK / 16],
+                                             float zscale, RowState<DK, DV, NW>& rs) {
   using C = Cfg<DK, DV, NW>;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
-  // ---- S^T = C . Q^T
+  // ---- S^T = C . Q^T, A operands prefetched kLookA steps ahead
+  // Lane (row col, half) reads logical piece 2*ks + half of its row.  The
+  // swizzle only flips the low two bits of the piece index, so every part-A
+  // address is one of two per-lane bases plus a compile-time offset.
+  const int sw = swz_a(col);
+  const uint16_t* a_even = tb + (col * C::kRA + (half ^ sw)) * 8;         // ks even
+  const uint16_t* a_odd = tb + (col * C::kRA + ((2 + half) ^ sw)) * 8;    // ks odd
+  auto load_a = [&](int ks) {
+    if (2 * ks < C::kPA) return *(const v8bf*)((ks & 1 ? a_odd : a_even) + 32 * (ks >> 1));
+    return *(const v8bf*)(tb + piece_pos<DK, DV, NW>(col, 2 * ks + half));
+  };
   v16f st = {};
-  const int wave = threadIdx.x >> 6;
+  v8bf abuf[kLookA];
 #pragma unroll
-  for (int ks = 0; ks < C::kKSL; ++ks) {
-    const v8bf av = *(const v8bf*)(tb + col * C::kRS + 16 * ks + 8 * half);
-    const v8bf bv = *(const v8bf*)(qlds + ((ks * 2 + half) * C::kHeads + wave * 32 + col) * 8);
-    st = mfma_bf16_32x32x16(av, bv, st);
-  }
+  for (int j = 0; j < kLookA; ++j) abuf[j] = load_a(j);
 #pragma unroll
-  for (int ks = 0; ks < C::kKSR; ++ks) {
-    const v8bf av = *(const v8bf*)(tb + col * C::kRS + 16 * (C::kKSL + ks) + 8 * half);
-    st = mfma_bf16_32x32x16(av, qb[ks], st);
+  for (int ks = 0; ks < C::kKS; ++ks) {
+    const v8bf cur = abuf[ks % kLookA];
+    if (ks + kLookA < C::kKS) abuf[ks % kLookA] = load_a(ks + kLookA);
+    st = mfma_bf16_32x32x16(cur, qb[ks], st);
   }
   // ---- mask, scale, chunk max
+  const uint32_t vh = valid >> (4 * half);
+  const bool all_valid = valid == 0xFFFFFFFFu;
   float z[16];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int r = 8 * (j >> 2) + 4 * half + (j & 3);
-    z[j] = sidx_c[r] >= 0 ? st[j] * zscale : -INFINITY;
+    const int r = 8 * (j >> 2) + (j & 3);       // row minus 4*half
+    z[j] = (all_valid || ((vh >> r) & 1u)) ? st[j] * zscale : -INFINITY;
     mx = fmaxf(mx, z[j]);
   }
   mx = max_halves(mx);
@@ -125,33 +182,56 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* tb, const int32_t* 
   v8bf pb[2];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float pj = exp2f(z[j] - rs.m_ref);
+    const float pj = __builtin_amdgcn_exp2f(z[j] - rs.m_ref);
     rs.l_sum += pj;
     pb[j >> 3][j & 7] = (__bf16)pj;
   }
   // ---- O^T += V^T . P^T ; K index k of step kk is row 16*kk + 8*((k%8)/4) + 4*(k/8) + k%4
+  // V^T operand of MFMA m (dim tile m/2, K step m%2): lane l needs dim
+  // 32t + l%32 at rows 16kk + 4*half + {0..3} (elements 0..3) and
+  // 16kk + 8 + 4*half + {0..3} (elements 4..7).  Two transposed reads: lane
+  // j of each 16-lane group addresses row (j/4) of the 4-row block at the
+  // 4 dims 4*(j%4) of its 16-dim slice.
+  // Rows 16kk + 4*half + jl/4 (+8) all share swz_a, so a 64-byte block of
+  // 4 pieces stays contiguous; the 4-dim group 4*(jl%4) sits in piece
+  // 4t + 2*(g%2) + (jl%4)/2 at element offset 4*(jl%2).
+  const int g = lane >> 4, jl = lane & 15;
+  const int vrow = 4 * (g >> 1) + (jl >> 2);      // + 16*kk (+ 8 for the high half)
+  const int vpiece = 2 * (g & 1) + ((jl & 3) >> 1);
+  const int vsub = 4 * (jl & 1);
+  // swz_a(16*kk + vrow) does not depend on kk, and the swizzle stays inside
+  // the 4-piece group, so addresses are two bases plus compile-time offsets.
+  const uint16_t* v_lo = tb + (vrow * C::kRA + (vpiece ^ swz_a(vrow))) * 8 + vsub;
+  const uint16_t* v_hi = tb + ((vrow + 8) * C::kRA + (vpiece ^ swz_a(vrow + 8))) * 8 + vsub;
+  auto load_v = [&](int m) {
+    const int t = m >> 1, kk = m & 1;
+    const int off = 16 * kk * C::kRA * 8 + 32 * t;
+    const v4bf lo = lds_read_tr16(v_lo + off);
+    const v4bf hi = lds_read_tr16(v_hi + off);
+    return (v8bf)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  constexpr int kM = 2 * C::kNT;
+  v8bf vbuf[kLookV];
 #pragma unroll
-  for (int t = 0; t < C::kNT; ++t) {
+  for (int j = 0; j < kLookV; ++j) vbuf[j] = load_v(j);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v8bf vv;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int r = 16 * kk + 8 * (jj >> 2) + 4 * half + (jj & 3);
-        vv[jj] = __builtin_bit_cast(__bf16, tb[r * C::kRS + 32 * t + col]);
-      }
-      rs.o[t] = mfma_bf16_32x32x16(vv, pb[kk], rs.o[t]);
-    }
+  for (int m = 0; m < kM; ++m) {
+    const v8bf cur = vbuf[m % kLookV];
+    if (m + kLookV < kM) vbuf[m % kLookV] = load_v(m + kLookV);
+    rs.o[m >> 1] = mfma_bf16_32x32x16(cur, pb[m & 1], rs.o[m >> 1]);
   }
 }
 
 template <int DK, int DV, int NW>
 __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   using C = Cfg<DK, DV, NW>;
+  // Three LDS tiles as separate objects so the compiler can tell the tile
+  // being read from the tiles being filled by DMA.
   __shared__ __attribute__((aligned(16))) uint16_t tile0[C::kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t tile1[C::kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[C::kQElems];
+  __shared__ __attribute__((aligned(16))) uint16_t tile2[C::kTileElems];
   __shared__ int32_t sidx[kMaxSlots];
+  __shared__ int redo;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -178,26 +258,19 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
     sidx[j] = v;
   }
 
-  // Q^T operand for the whole row: K steps [0, kKSL) of all heads in LDS,
-  // laid out [ks][half][head][8] so a wave's 16-byte reads are consecutive;
-  // K steps [kKSL, kKS) of this wave's 32 heads in registers.
-  for (int pc = threadIdx.x; pc < C::kKSL * 2 * C::kHeads; pc += C::kThreads) {
-    const int hh = pc % C::kHeads, kh = pc / C::kHeads;   // kh = ks * 2 + half
-    v8bf v = {};
-    if (hh < a.H) v = *(const v8bf*)(a.q + (qrow * a.H + hh) * DK + 8 * kh);
-    *(v8bf*)(qlds + pc * 8) = v;
-  }
+  // Q^T operand of this wave's 32 heads, kept in registers for the whole row.
   const int h = wave * 32 + col;
-  v8bf qb[C::kKSR];
+  v8bf qb[C::kKS];
   {
-    const uint16_t* qp = a.q + (qrow * a.H + min(h, a.H - 1)) * DK + 16 * C::kKSL + 8 * half;
+    const uint16_t* qp = a.q + (qrow * a.H + min(h, a.H - 1)) * DK + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < C::kKSR; ++ks) {
+    for (int ks = 0; ks < C::kKS; ++ks) {
       v8bf v = *(const v8bf*)(qp + 16 * ks);
       if (h >= a.H) v = (v8bf){};
       qb[ks] = v;
     }
   }
+  wait_vm<0>();
   __syncthreads();
 
   const uint16_t* kvb = a.kv + (int64_t)b * a.S * DK;
@@ -205,38 +278,45 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   rs.m_ref = -INFINITY;
   rs.m_seen = -INFINITY;
   const float zscale = a.sm_scale * kLog2e;
-  __shared__ int redo;
+  constexpr int ndma = C::kDma / NW;   // DMA instructions per wave per chunk
 
-  auto chunk_valid = [&](int c) {
-    return __builtin_amdgcn_ballot_w64(lane < kChunk && sidx[c * kChunk + (lane & 31)] >= 0) != 0;
+  // Chunk c lives in tile c % 3.  DMA for chunk c+2 is issued once every wave
+  // has passed the barrier of chunk c (so nobody still reads chunk c-1's
+  // tile); before that barrier each wave waits until its own part of chunk c
+  // has landed while chunk c+1's DMA stays in flight.
+  auto step = [&](int c, const uint16_t* cur, uint16_t* fill) {
+    if (c + 1 < nchunks) wait_vm<ndma>(); else wait_vm<0>();
+    // A bare barrier: __syncthreads() would add a release fence that waits
+    // for every outstanding DMA, including the chunks being prefetched.
+    // Chunk c's tile is complete once every wave passed its wait above, and
+    // the tile refilled next was last read (and consumed) in chunk c-1.
+    __builtin_amdgcn_s_barrier();
+    if (c + 2 < nchunks) gather_dma<DK, DV, NW>(fill, kvb, sidx[(c + 2) * kChunk + (lane & 31)]);
+    const uint32_t valid =
+        (uint32_t)__builtin_amdgcn_ballot_w64(lane < kChunk && sidx[c * kChunk + (lane & 31)] >= 0);
+    if (valid != 0u) attend_chunk<DK, DV, NW>(cur, valid, qb, zscale, rs);
   };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int t = 0; t < C::kNT; ++t) rs.o[t] = (v16f){};
     rs.l_sum = 0.f;
-    if (threadIdx.x == 0) redo = 0;
-    // Double buffering: chunk c is read from tile(c%2) while chunk c+1 is
-    // DMA'd into the other tile; one barrier per chunk.
-    if (nchunks > 0) gather_dma<DK, DV, NW>(tile0, kvb, sidx);
-    wait_dma();
-    __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) gather_dma<DK, DV, NW>(tile1, kvb, sidx + (c + 1) * kChunk);
-      if (chunk_valid(c)) attend_chunk<DK, DV, NW>(tile0, sidx + c * kChunk, qlds, qb, zscale, rs);
-      wait_dma();
-      __syncthreads();
+    if (nchunks > 0) gather_dma<DK, DV, NW>(tile0, kvb, sidx[lane & 31]);
+    if (nchunks > 1) gather_dma<DK, DV, NW>(tile1, kvb, sidx[kChunk + (lane & 31)]);
+    for (int c = 0; c < nchunks; c += 3) {
+      step(c, tile0, tile2);
       if (c + 1 >= nchunks) break;
-      if (c + 2 < nchunks) gather_dma<DK, DV, NW>(tile0, kvb, sidx + (c + 2) * kChunk);
-      if (chunk_valid(c + 1)) attend_chunk<DK, DV, NW>(tile1, sidx + (c + 1) * kChunk, qlds, qb, zscale, rs);
-      wait_dma();
-      __syncthreads();
+      step(c + 1, tile1, tile0);
+      if (c + 2 >= nchunks) break;
+      step(c + 2, tile2, tile1);
     }
     // A logit far above its head's reference: redo the row with the true max.
+    if (threadIdx.x == 0) redo = 0;
+    __syncthreads();
     if (rs.m_seen > rs.m_ref + kRefHeadroom) redo = 1;
     __syncthreads();
     if (!redo) break;
     rs.m_ref = rs.m_seen;
-    __syncthreads();
   }
 
   // ---- epilogue
