@@ -21,6 +21,8 @@
 //    each 16-lane row ends with one query's 16 scores.
 //  * decode: a wave keeps one row's q and streams 4 key tiles per step; the
 //    reduce-scatter leaves 64 consecutive keys' scores, one per lane.
+#include <climits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -29,123 +31,392 @@ namespace {
 
 constexpr int kMaxHeadTiles = 4;   // H_I <= 64
 
-// A operand: 16 heads x 128 bytes of one query row (zero outside H_I/d_I).
-__device__ __forceinline__ v8i load_q_tile(const IndexerArgs& a, int b, int i, int ht, int lane) {
-  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int h = ht * 16 + (lane & 15);
-  const int off = 32 * (lane >> 4);
-  if (i < a.rows && h < a.HI) {
-    const uint8_t* base = a.q_idx + (((int64_t)b * a.qrows_b + i) * a.HI + h) * a.dI + off;
-    if (off + 16 <= a.dI) {
-      const u32x4 x = *(const u32x4*)base;
-      r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
-    }
-    if (off + 32 <= a.dI) {
-      const u32x4 x = *(const u32x4*)(base + 16);
-      r[4] = x[0]; r[5] = x[1]; r[6] = x[2]; r[7] = x[3];
-    }
-  }
-  return r;
+// 16 bytes of a row of FP8 codes at byte offset `off` (zero if off >= len).
+// Branch-free: the address is clamped inside the row and the value masked.
+__device__ __forceinline__ u32x4 load16_or_zero(const uint8_t* row, int off, int len, bool ok) {
+  const bool in = ok && off < len;
+  const u32x4 x = *(const u32x4*)(row + min(off, len - 16));
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return in ? x : z;
 }
 
-// B operand: 16 keys x 128 bytes; lane holds key s (zero if s >= S).
-__device__ __forceinline__ v8i load_k_tile(const IndexerArgs& a, int b, int s, int lane) {
-  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+// A operand: 16 heads x 128 bytes of one query row (zero outside H_I/d_I).
+// Lane l holds head 16*ht + l%16, bytes [32*(l/16), 32*(l/16) + 32).
+__device__ __forceinline__ v8i load_q_tile(const IndexerArgs& a, int b, int i, int ht, int lane) {
+  const int h = ht * 16 + (lane & 15);
   const int off = 32 * (lane >> 4);
-  if (s < a.S) {
-    const uint8_t* base = a.k_idx + ((int64_t)b * a.S + s) * a.dI + off;
-    if (off + 16 <= a.dI) {
-      const u32x4 x = *(const u32x4*)base;
-      r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
-    }
-    if (off + 32 <= a.dI) {
-      const u32x4 x = *(const u32x4*)(base + 16);
-      r[4] = x[0]; r[5] = x[1]; r[6] = x[2]; r[7] = x[3];
-    }
+  const bool ok = i < a.rows && h < a.HI;
+  const uint8_t* row = a.q_idx + (((int64_t)b * a.qrows_b + min(i, a.rows - 1)) * a.HI + min(h, a.HI - 1)) * a.dI;
+  const u32x4 lo = load16_or_zero(row, off, a.dI, ok), hi = load16_or_zero(row, off + 16, a.dI, ok);
+  return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Streaming form of the B operand for the key loops: `kb` is the sequence's
+// key base (uniform), `lane_off` = min(32*(lane/16), d_I-16) and `dmask`
+// says whether the lane's K bytes exist (d_I < 128 pads with zero).  Keys
+// at or beyond S read key S-1 instead; their results are never stored (each
+// score column depends only on its own key), so no zeroing is needed.
+template <bool kFullD>
+struct KeyStream {
+  const uint8_t* kb;
+  int dI, smax, lane_off;
+  bool lo_ok, hi_ok;
+  __device__ __forceinline__ void init(const IndexerArgs& a, int b, int lane) {
+    kb = a.k_idx + (int64_t)b * a.S * a.dI;
+    dI = a.dI;
+    smax = a.S - 1;
+    const int off = 32 * (lane >> 4);
+    lane_off = min(off, a.dI - 16);
+    lo_ok = off < a.dI;
+    hi_ok = off + 16 < a.dI;
   }
-  return r;
+  __device__ __forceinline__ v8i load(int s) const {
+    if constexpr (kFullD) {   // d_I = 128: every lane's 32 bytes exist
+      const uint32_t o = (uint32_t)(min(s, smax) * 128 + lane_off);
+      const u32x4 lo = *(const u32x4*)(kb + o);
+      const u32x4 hi = *(const u32x4*)(kb + o + 16);
+      return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    const uint32_t o = (uint32_t)(min(s, smax) * dI + lane_off);
+    const u32x4 lo = *(const u32x4*)(kb + o);
+    const u32x4 hi = *(const u32x4*)(kb + o + (hi_ok ? 16 : 0));
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 l = lo_ok ? lo : z, h = hi_ok ? hi : z;
+    return (v8i){(int)l[0], (int)l[1], (int)l[2], (int)l[3], (int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+  }
+};
+
+__device__ __forceinline__ float load_k_scale(const IndexerArgs& a, int b, int s) {
+  const float v = a.k_scale[(int64_t)b * a.S + min(s, a.S - 1)];
+  return s < a.S ? v : 0.f;
 }
 
 // Folded head weights w[t,j]*qs[t] for the 4 heads (per head tile) this lane
 // sees in the MFMA result: head 16*ht + 4*(lane/16) + r.
 __device__ __forceinline__ void load_weights(const IndexerArgs& a, int b, int i, int lane,
                                              float (&wq)[kMaxHeadTiles][4]) {
+  // Branch-free: clamped indices, then masks, so all loads are in flight at once.
   const bool row_ok = i < a.rows;
-  const int64_t row = (int64_t)b * a.qrows_b + i;
+  const int64_t row = (int64_t)b * a.qrows_b + min(i, a.rows - 1);
   const float qs = row_ok ? a.q_scale[row] : 0.f;
+  const uint16_t* wr = a.w + row * a.HI;
 #pragma unroll
   for (int ht = 0; ht < kMaxHeadTiles; ++ht)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 16 * ht + 4 * (lane >> 4) + r;
-      wq[ht][r] = (row_ok && h < a.HI) ? bf16_to_f32(a.w[row * a.HI + h]) * qs : 0.f;
+      const float wv = bf16_to_f32(wr[min(h, a.HI - 1)]);
+      wq[ht][r] = (row_ok && h < a.HI) ? wv * qs : 0.f;
     }
 }
 
-// Partial head sum of one query row against one 16-key tile: this lane's
-// 16 heads (4 per head tile), sum_h wq[h] * ReLU(dot_h), in a fixed order.
-__device__ __forceinline__ float tile_partial(const v8i (&qa)[kMaxHeadTiles], const float (&wq)[kMaxHeadTiles][4],
-                                              const v8i& kt, int n_head_tiles) {
-  float acc = 0.f;
+// max(x, 0) as one integer max on the bit pattern: negative floats (and
+// -0.0) are negative as int32, positive ones keep their bits.  fmaxf would
+// first canonicalise the MFMA result (one more VALU op per element).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Four partial head sums: for u = 0..3, the MFMA products of query operand
+// set qa[u] (NHT head tiles) with key tile kt[u], followed by this lane's
+// sum_h wq[u][h] * ReLU(dot) in the fixed order ht = 0..NHT-1, r = 0..3.
+// The MFMAs are issued head-tile-major and each result's epilogue runs four
+// MFMAs after it was issued, so the matrix core and the VALU work overlap
+// within one wave (1 MFMA : 8 VALU is the balanced ratio for this tile).
+template <int NHT>
+__device__ __forceinline__ void tile_partials(const v8i* const (&qa)[4], const float (*const (&wq)[4])[4],
+                                              const v8i* const (&kt)[4], float (&acc)[4]) {
+  v4f d[NHT][4];
 #pragma unroll
-  for (int ht = 0; ht < kMaxHeadTiles; ++ht) {
-    if (ht < n_head_tiles) {
-      const v4f d = mfma_fp8_16x16x128(qa[ht], kt);
+  for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc = fmaf(wq[ht][r], fmaxf(d[r], 0.f), acc);
-    }
+    for (int u = 0; u < 4; ++u) d[ht][u] = mfma_fp8_16x16x128(qa[u][ht], *kt[u]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[u] = fmaf(wq[u][ht][r], relu_bits(d[ht][u][r]), acc[u]);
+  // schedule: pending LDS reads (the next step's operands, if any) first,
+  // then 4 MFMAs, then (1 MFMA, 8 VALU) pairs, then the tail
+  __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+  for (int k = 0; k < 4 && k < 4 * NHT; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+  for (int k = 4; k < 4 * NHT; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
   }
-  return acc;
+  __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
 }
 
 constexpr int kPrefillWaves = 8;
-constexpr int kRowsPerWave = 4;
-constexpr int kPrefillRows = kPrefillWaves * kRowsPerWave;   // 32 query rows per workgroup
+constexpr int kRowsPerWave = 2;
+constexpr int kPrefillRows = kPrefillWaves * kRowsPerWave;   // 16 query rows per workgroup
 
+// Work tile = (16 query rows, keys_per_wg keys) of one sequence; each wave
+// owns 2 rows and consumes two 16-key tiles per step (the four partials of
+// a step are (row, tile) pairs).  Tiles are numbered so that the workgroups
+// of one XCD (dispatch goes round-robin over the 8 XCDs) share key blocks:
+// tile id -> xcd = id % 8, then q-block fastest within the XCD, and the
+// XCD's key blocks are kb = 8 * j + xcd.
+template <int NHT, bool kFullD>
 __global__ void __launch_bounds__(kPrefillWaves * kWave)
-indexer_prefill_kernel(IndexerArgs a, int keys_per_wg) {
+indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int b = blockIdx.z;
-  const int i0 = blockIdx.y * kPrefillRows + wave * kRowsPerWave;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, jx = id >> 3;
+  const int qb = jx % nqb;
+  const int kb = (jx / nqb) * 8 + xcd;
+  const int b = blockIdx.y;
+  const int i0 = qb * kPrefillRows + wave * kRowsPerWave;
   if (i0 >= a.rows) return;
   const int i_last = min(i0 + kRowsPerWave, a.rows) - 1;
   const int np_last = min(a.pos0 + i_last + 1, a.S);
-  const int k_begin = blockIdx.x * keys_per_wg;
+  const int k_begin = kb * keys_per_wg;
   const int k_end = min(k_begin + keys_per_wg, np_last);
   if (k_begin >= k_end) return;
-  const int nht = (a.HI + 15) >> 4;
 
   v8i qa[kRowsPerWave][kMaxHeadTiles];
   float wq[kRowsPerWave][kMaxHeadTiles][4];
 #pragma unroll
   for (int q = 0; q < kRowsPerWave; ++q) {
 #pragma unroll
-    for (int ht = 0; ht < kMaxHeadTiles; ++ht) qa[q][ht] = load_q_tile(a, b, i0 + q, ht, lane);
+    for (int ht = 0; ht < NHT; ++ht) qa[q][ht] = load_q_tile(a, b, i0 + q, ht, lane);
     load_weights(a, b, i0 + q, lane, wq[q]);
   }
-  // This lane stores the scores of query row i0 + lane/16.
-  const int my_row = i0 + (lane >> 4);
+  // After the reduce-scatter, lane group g holds row i0 + g/2, tile g%2.
+  const int g = lane >> 4;
+  const int my_row = i0 + (g >> 1);
   const int my_np = my_row < a.rows ? min(a.pos0 + my_row + 1, a.S) : 0;
   float* my_out = a.scores + ((int64_t)b * a.sc_rows_b + min(my_row, a.rows - 1)) * a.ld;
+  const v8i* qp[4] = {qa[0], qa[0], qa[1], qa[1]};
+  const float(*wp[4])[4] = {wq[0], wq[0], wq[1], wq[1]};
 
-  v8i kt = load_k_tile(a, b, k_begin + (lane & 15), lane);
-  for (int s0 = k_begin; s0 < k_end; s0 += 16) {
-    const int s = s0 + (lane & 15);
-    const float ks = s < a.S ? a.k_scale[(int64_t)b * a.S + s] : 0.f;
-    const v8i kt_next = (s0 + 16 < k_end) ? load_k_tile(a, b, s + 16, lane) : kt;
-    float p[kRowsPerWave];
-#pragma unroll
-    for (int q = 0; q < kRowsPerWave; ++q) p[q] = tile_partial(qa[q], wq[q], kt, nht);
+  KeyStream<kFullD> ksr;
+  ksr.init(a, b, lane);
+  const int kl = lane & 15;
+  v8i kt0 = ksr.load(k_begin + kl);
+  v8i kt1 = ksr.load(k_begin + 16 + kl);
+  for (int s0 = k_begin; s0 < k_end; s0 += 32) {
+    const int s = s0 + 16 * (g & 1) + kl;   // key this lane's result belongs to
+    const float ks = load_k_scale(a, b, s);
+    // next step's tiles (past the block: harmless extra loads)
+    const v8i n0 = ksr.load(s0 + 32 + kl);
+    const v8i n1 = ksr.load(s0 + 48 + kl);
+    const v8i* kp[4] = {&kt0, &kt1, &kt0, &kt1};
+    float p[4];
+    tile_partials<NHT>(qp, wp, kp, p);
     const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
-    if (s < my_np) my_out[s] = tot * ks;
-    kt = kt_next;
+    if (s < my_np && s < k_end) my_out[s] = tot * ks;
+    kt0 = n0;
+    kt1 = n1;
   }
+}
+
+// Same work tile for d_I = 128, with the key block streamed through LDS in
+// sub-blocks of 256 keys (32 KB + 1 KB of scales).  Two buffers are filled
+// by global_load_lds DMA a whole sub-block ahead, so each key tile is read
+// from memory once per workgroup and the loads are long done when needed.
+// Key k of a sub-block occupies 128 bytes; its 16-byte piece p is stored at
+// position p ^ f(k), f(k) = (k % 8) ^ ((k / 8) % 2): any 8 consecutive keys
+// then hit 8 distinct 16-byte bank groups, and any 16 consecutive keys all
+// 64 banks, so the B-operand reads are conflict-free whether the LDS serves
+// 8 or 16 lanes of a ds_read_b128 per cycle.
+//
+// The B operands of step st+1 are read from LDS while step st's MFMAs run
+// (two register sets alternate with the step parity).  The per-score
+// arithmetic is tile_partials', as in every other indexer path.  NW = 4
+// waves per workgroup lets two workgroups share a CU, so one's barrier
+// waits and prologue are covered by the other's work.
+//
+// LDS DMA (global_load_lds) issued from inline asm: each lane copies 16
+// (or 4) bytes from `src` to lds_base + 16*lane (4*lane).  The compiler's
+// wait insertion cannot tell the two staging buffers apart and would make
+// every LDS read wait for all DMA in flight (including the prefetch into
+// the other buffer), so the copies are hidden from it and completion is
+// awaited explicitly with wait_dma() before the barrier that publishes a
+// buffer.  M0 is saved and restored around the copy.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+__device__ __forceinline__ void dma_x4(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma_x1(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+constexpr int kSubKeys = 256;
+constexpr int kSubBytes = kSubKeys * 128;
+constexpr int kLdsWaves = 4;
+constexpr int kLdsRows = kLdsWaves * kRowsPerWave;   // 8 query rows per workgroup
+
+// At least 2 waves per SIMD: caps the registers at 256 per lane, which also
+// keeps the MFMA results in VGPRs where the epilogue reads them directly.
+template <int NHT, int NW>
+__global__ void __launch_bounds__(NW * kWave, 2)
+indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
+  constexpr int kRows = NW * kRowsPerWave;
+  static_assert(32 % NW == 0 && NW >= 4, "DMA split");
+  // Two separate arrays (not one indexed array), so that the compiler can
+  // tell LDS reads of one buffer from the DMA in flight into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf0[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf1[kSubBytes];
+  __shared__ __attribute__((aligned(16))) float sbuf0[kSubKeys];
+  __shared__ __attribute__((aligned(16))) float sbuf1[kSubKeys];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the store descriptor scalar
+  const int id = blockIdx.x;
+  const int xcd = id & 7, jx = id >> 3;
+  const int qb = jx % nqb;
+  const int kb = (jx / nqb) * 8 + xcd;
+  const int b = blockIdx.y;
+  const int i0 = qb * kRows + wave * kRowsPerWave;
+  // Block-uniform extent: every wave takes part in the DMA and barriers.
+  if (qb * kRows >= a.rows) return;
+  const int blk_last = min(qb * kRows + kRows, a.rows) - 1;
+  const int k_begin = kb * keys_per_wg;
+  const int k_end = min(k_begin + keys_per_wg, min(a.pos0 + blk_last + 1, a.S));
+  if (k_begin >= k_end) return;
+  const int nsteps = (k_end - k_begin + 31) / 32;   // 32 keys per step, 8 steps per sub-block
+  const int nsub = (nsteps + 7) / 8;
+
+  const uint8_t* kseq = a.k_idx + (int64_t)b * a.S * 128;
+  const float* sseq = a.k_scale + (int64_t)b * a.S;
+  // DMA of sub-block j: wave w issues the 1 KB runs NW*u + w (8 keys each);
+  // waves 0..3 also copy 64 key scales each.
+  auto dma = [&](int j, uint8_t* kdst, float* sdst) {
+    const int key0 = k_begin + j * kSubKeys;
+#pragma unroll
+    for (int u = 0; u < 32 / NW; ++u) {
+      const int inst = u * NW + wave;
+      const int kl = inst * 8 + (lane >> 3);   // key within the sub-block
+      const int ppos = lane & 7;               // stored piece position
+      const int key = min(key0 + kl, a.S - 1);
+      const uint8_t* src = kseq + (int64_t)key * 128 + 16 * (ppos ^ ((kl & 7) ^ ((kl >> 3) & 1)));
+      dma_x4(src, lds_addr(kdst + inst * 1024));
+    }
+    if (wave < 4) {
+      const int skey = min(key0 + 64 * wave + lane, a.S - 1);
+      dma_x1(sseq + skey, lds_addr(sdst + 64 * wave));
+    }
+  };
+  dma(0, kbuf0, sbuf0);
+
+  v8i qa[kRowsPerWave][kMaxHeadTiles];
+  float wq[kRowsPerWave][kMaxHeadTiles][4];
+#pragma unroll
+  for (int q = 0; q < kRowsPerWave; ++q) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) qa[q][ht] = load_q_tile(a, b, i0 + q, ht, lane);
+    load_weights(a, b, i0 + q, lane, wq[q]);
+  }
+  // After the reduce-scatter, lane group g holds row i0 + g/2, key tile g%2.
+  const int g = lane >> 4;
+  const int kl16 = lane & 15;
+  const int my_row = i0 + (g >> 1);
+  const int my_np = min(my_row < a.rows ? min(a.pos0 + my_row + 1, a.S) : 0, k_end);
+  // Scores go out through a raw buffer store whose range covers this wave's
+  // rows: a lane with nothing to store uses an offset past the range, which
+  // the hardware drops, so the step loop has no divergent branch.
+  // A wave whose rows all lie past the end (ragged last workgroup) gets an
+  // empty range.  The launcher guarantees 2*ld + S fits the 31-bit offsets.
+  const int64_t wave_row0 = (int64_t)b * a.sc_rows_b + min(i0, a.rows - 1);
+  const int nrows_w = max(0, min(kRowsPerWave, a.rows - i0));
+  const int range = nrows_w > 0 ? (int)((int64_t)(nrows_w - 1) * a.ld * 4 + (int64_t)a.S * 4) : 0;
+  const __amdgpu_buffer_rsrc_t out_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(a.scores + wave_row0 * a.ld, 0, range, 0x00020000);
+  const int lane_row_off = (my_row - i0) * (int)a.ld * 4;
+  const v8i* qp[4] = {qa[0], qa[0], qa[1], qa[1]};
+  const float(*wp[4])[4] = {wq[0], wq[0], wq[1], wq[1]};
+
+  // B operands of a step (tiles 2*sst and 2*sst+1 of a staged sub-block)
+  // and the scale of the key this lane's result of the step belongs to.
+  auto read_step = [&](const uint8_t* kbf, const float* sbf, int sst, v8i& t0, v8i& t1, float& ks) {
+    const int k0 = 32 * sst + kl16;
+    const int k1 = k0 + 16;
+    const int f0 = (k0 & 7) ^ ((k0 >> 3) & 1), f1 = (k1 & 7) ^ ((k1 >> 3) & 1);
+    const u32x4 a0 = *(const u32x4*)(kbf + k0 * 128 + 16 * ((2 * g) ^ f0));
+    const u32x4 a1 = *(const u32x4*)(kbf + k0 * 128 + 16 * ((2 * g + 1) ^ f0));
+    const u32x4 b0 = *(const u32x4*)(kbf + k1 * 128 + 16 * ((2 * g) ^ f1));
+    const u32x4 b1 = *(const u32x4*)(kbf + k1 * 128 + 16 * ((2 * g + 1) ^ f1));
+    t0 = (v8i){(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    t1 = (v8i){(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    ks = sbf[32 * sst + 16 * (g & 1) + kl16];
+  };
+
+  // One step: the MFMAs and epilogue of step st with operands (kt0, kt1,
+  // ks) while the operands of step st+1 are read from (nk, ns) at
+  // sub-block step nsst into (nt0, nt1, nks).
+  auto body = [&](int st, const v8i& kt0, const v8i& kt1, float ks, const uint8_t* nk, const float* ns, int nsst,
+                  v8i& nt0, v8i& nt1, float& nks) {
+    read_step(nk, ns, nsst, nt0, nt1, nks);
+    const v8i* kp[4] = {&kt0, &kt1, &kt0, &kt1};
+    float p[4];
+    tile_partials<NHT>(qp, wp, kp, p);
+    const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
+    const int s = k_begin + 32 * st + 16 * (g & 1) + kl16;
+    const int off = s < my_np ? lane_row_off + s * 4 : INT_MAX;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, off, 0, 0);
+  };
+  // The 8 steps of sub-block j from buffer (ck, cs); the last one reads the
+  // first operands of sub-block j+1 from (ok, os) after the barrier that
+  // publishes it, and then sub-block j+2 is sent into (ck, cs).  Register
+  // sets A/B alternate with the step parity (sub-blocks start even).
+  v8i ktA0, ktA1, ktB0, ktB1;
+  float ksA, ksB;
+  auto sub_block = [&](int j, uint8_t* ck, float* cs, uint8_t* ok, float* os) {
+    const int st0 = 8 * j;
+#pragma unroll
+    for (int sst = 0; sst < 8; sst += 2) {
+      if (st0 + sst >= nsteps) return;
+      if (sst == 6) {
+        body(st0 + 6, ktA0, ktA1, ksA, ck, cs, 7, ktB0, ktB1, ksB);
+        if (st0 + 7 >= nsteps) return;
+        wait_dma();
+        __syncthreads();   // sub-block j+1 staged; everyone is done reading buffer (ck, cs)
+        if (j + 2 < nsub) dma(j + 2, ck, cs);
+        body(st0 + 7, ktB0, ktB1, ksB, ok, os, 0, ktA0, ktA1, ksA);
+      } else {
+        body(st0 + sst, ktA0, ktA1, ksA, ck, cs, sst + 1, ktB0, ktB1, ksB);
+        if (st0 + sst + 1 >= nsteps) return;
+        body(st0 + sst + 1, ktB0, ktB1, ksB, ck, cs, sst + 2, ktA0, ktA1, ksA);
+      }
+    }
+  };
+
+  // Consume the q and weight loads here, so that the compiler's waits for
+  // them do not end up behind (and wait for) the next DMA.
+#pragma unroll
+  for (int q = 0; q < kRowsPerWave; ++q)
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      asm volatile("" ::"v"(qa[q][ht]));
+      asm volatile("" ::"v"(wq[q][ht][0]), "v"(wq[q][ht][1]), "v"(wq[q][ht][2]), "v"(wq[q][ht][3]));
+    }
+  wait_dma();
+  __syncthreads();   // sub-block 0 staged
+  if (nsub > 1) dma(1, kbuf1, sbuf1);
+  read_step(kbuf0, sbuf0, 0, ktA0, ktA1, ksA);
+  for (int j = 0; j < nsub; j += 2) {
+    sub_block(j, kbuf0, sbuf0, kbuf1, sbuf1);
+    if (j + 1 >= nsub) break;
+    sub_block(j + 1, kbuf1, sbuf1, kbuf0, sbuf0);
+  }
+  wait_dma();   // nothing may still write this workgroup's LDS after it ends
 }
 
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeKeysPerWave = 512;
 
+template <int NHT, bool kFullD>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
 indexer_decode_kernel(IndexerArgs a) {
   const int lane = threadIdx.x & 63;
@@ -156,28 +427,31 @@ indexer_decode_kernel(IndexerArgs a) {
   const int k_begin = (blockIdx.x * kDecodeWaves + wave) * kDecodeKeysPerWave;
   if (k_begin >= np) return;
   const int k_end = min(k_begin + kDecodeKeysPerWave, np);
-  const int nht = (a.HI + 15) >> 4;
 
   v8i qa[kMaxHeadTiles];
   float wq[kMaxHeadTiles][4];
 #pragma unroll
-  for (int ht = 0; ht < kMaxHeadTiles; ++ht) qa[ht] = load_q_tile(a, b, i, ht, lane);
+  for (int ht = 0; ht < NHT; ++ht) qa[ht] = load_q_tile(a, b, i, ht, lane);
   load_weights(a, b, i, lane, wq);
   float* out = a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld;
+  const v8i* qp[4] = {qa, qa, qa, qa};
+  const float(*wp[4])[4] = {wq, wq, wq, wq};
 
+  KeyStream<kFullD> ksr;
+  ksr.init(a, b, lane);
+  const int kl = lane & 15;
   v8i kt[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) kt[u] = load_k_tile(a, b, k_begin + 16 * u + (lane & 15), lane);
+  for (int u = 0; u < 4; ++u) kt[u] = ksr.load(k_begin + 16 * u + kl);
   for (int s0 = k_begin; s0 < k_end; s0 += 64) {
     const int s = s0 + lane;   // key whose score this lane ends up holding
-    const float ks = s < a.S ? a.k_scale[(int64_t)b * a.S + s] : 0.f;
+    const float ks = load_k_scale(a, b, s);
     v8i nx[4];
-    const bool more = s0 + 64 < k_end;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) nx[u] = more ? load_k_tile(a, b, s0 + 64 + 16 * u + (lane & 15), lane) : kt[u];
+    for (int u = 0; u < 4; ++u) nx[u] = ksr.load(s0 + 64 + 16 * u + kl);
+    const v8i* kp[4] = {&kt[0], &kt[1], &kt[2], &kt[3]};
     float p[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) p[u] = tile_partial(qa, wq, kt[u], nht);
+    tile_partials<NHT>(qp, wp, kp, p);
     const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
     if (s < k_end) out[s] = tot * ks;
 #pragma unroll
@@ -185,29 +459,56 @@ indexer_decode_kernel(IndexerArgs a) {
   }
 }
 
-}  // namespace
+// The LDS-staged kernel stores through 31-bit byte offsets within two rows.
+bool lds_path_ok(const IndexerArgs& a) { return (2 * a.ld + (int64_t)a.S) * 4 < (int64_t)INT_MAX; }
 
-hipError_t launch_indexer(const IndexerArgs& a, bool decode_form, hipStream_t st) {
-  if (a.rows <= 0 || a.B <= 0) return hipSuccess;
+template <int NHT, bool kFullD>
+hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
   const int np_max = min(a.pos0 + a.rows, a.S);   // longest row
   if (decode_form) {
     const int per_wg = kDecodeWaves * kDecodeKeysPerWave;
     dim3 grid((np_max + per_wg - 1) / per_wg, a.rows, a.B);
-    hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(kDecodeWaves * kWave), 0, st, a);
+    hipLaunchKernelGGL((indexer_decode_kernel<NHT, kFullD>), grid, dim3(kDecodeWaves * kWave), 0, st, a);
   } else {
-    const int qblocks = (a.rows + kPrefillRows - 1) / kPrefillRows;
-    // Larger key blocks amortise the q loads (8 KB per row); smaller ones
-    // give enough workgroups for small problems.  Results do not depend on it.
+    const int rows_per_wg = (kFullD && lds_path_ok(a)) ? kLdsRows : kPrefillRows;
+    const int nqb = (a.rows + rows_per_wg - 1) / rows_per_wg;
+    // Large key blocks amortise the q loads (8 KB per row); smaller ones
+    // keep at least ~512 workgroups busy.  Results do not depend on it.
     int keys = 2048;
     while (keys > 256) {
       const long long kblocks = (np_max + keys - 1) / keys;
-      if ((long long)qblocks * kblocks * a.B >= 4096) break;
+      if ((long long)nqb * kblocks * a.B >= 512) break;
       keys >>= 1;
     }
-    dim3 grid((np_max + keys - 1) / keys, qblocks, a.B);
-    hipLaunchKernelGGL(indexer_prefill_kernel, grid, dim3(kPrefillWaves * kWave), 0, st, a, keys);
+    const int nkb = (np_max + keys - 1) / keys;
+    const int nkb8 = (nkb + 7) / 8;
+    dim3 grid((unsigned)(8 * nqb * nkb8), a.B);
+    if (kFullD && lds_path_ok(a))
+      hipLaunchKernelGGL((indexer_prefill_lds_kernel<NHT, kLdsWaves>), grid, dim3(kLdsWaves * kWave), 0, st, a, keys, nqb);
+    else
+      hipLaunchKernelGGL((indexer_prefill_kernel<NHT, kFullD>), grid, dim3(kPrefillWaves * kWave), 0, st, a, keys, nqb);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const IndexerArgs& a, bool decode_form, hipStream_t st) {
+  if (a.rows <= 0 || a.B <= 0) return hipSuccess;
+  if (a.dI == 128) {
+    switch ((a.HI + 15) >> 4) {
+      case 1: return launch_nht<1, true>(a, decode_form, st);
+      case 2: return launch_nht<2, true>(a, decode_form, st);
+      case 3: return launch_nht<3, true>(a, decode_form, st);
+      default: return launch_nht<4, true>(a, decode_form, st);
+    }
+  }
+  switch ((a.HI + 15) >> 4) {
+    case 1: return launch_nht<1, false>(a, decode_form, st);
+    case 2: return launch_nht<2, false>(a, decode_form, st);
+    case 3: return launch_nht<3, false>(a, decode_form, st);
+    default: return launch_nht<4, false>(a, decode_form, st);
+  }
 }
 
 }  // namespace dsa
