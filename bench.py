@@ -124,6 +124,45 @@ def time_stages(torch, wl, d, dsa, reps, stream):
     return {k2: v / reps for k2, v in tot.items()}, launches // reps, nws
 
 
+# Dominant-kernel names per stage, the rocprofv3 summary that holds its
+# measured HBM traffic, and the sources that summary was taken from.
+STAGE_KERNELS = {
+    "indexer": ("indexer_prefill_lds_kernel<4,4>", "indexer_prefill_lds_kernel_p128k.md", "indexer.hip"),
+    "attention": ("sparse_mla_kernel<576,512,4>", "sparse_mla_kernel_p128k.md", "sparse_mla.hip"),
+    "topk": ("topk_kernel", "topk_kernel_p128k.md", "topk.hip"),
+}
+
+
+def source_sha16(src):
+    import hashlib
+    h = hashlib.sha256()
+    for f in (src, "dsa_device.h", "dsa_internal.h"):
+        with open(os.path.join(ROOT, "sparse_attention_long_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(stage, workload):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None if there is none for this workload
+    or the kernel's sources changed since it was taken."""
+    if workload != "p128k":
+        return None
+    _, md, src = STAGE_KERNELS[stage]
+    path = os.path.join(ROOT, "profiles", md)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256_16"):
+                k, v = line.split(":", 1)
+                vals[k] = v.split()[0]
+    if vals.get("source_sha256_16") != source_sha16(src) or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(wl, n_rows):
     """The CPU oracle (unchanged) on a stratified sample of query rows:
     rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
@@ -162,6 +201,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=1)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size kernel that "
+                         "calibrates FETCH_SIZE/WRITE_SIZE counters in a rocprofv3 --pmc run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the DSA forward path here is a single-GPU build "
@@ -175,6 +217,15 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+        del src, dst
     log(f"[bench] filling {wl.name} inputs on the GPU")
     d = fill_inputs(wl)
     torch.cuda.synchronize()
@@ -194,18 +245,21 @@ def main():
     log(f"[bench] stages ms {stages}; indexer {idx_tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s, "
         f"top-k {topk_gbs:.0f} GB/s")
     dom = max(stages, key=stages.get)
+    kname = STAGE_KERNELS[dom][0]
     if dom == "indexer":
-        roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma", "achieved": idx_tflops,
+        roof = {"kernel": kname, "bound": "mfma", "achieved": idx_tflops,
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "dtype": "fp8"}
     elif dom == "attention":
-        roof = {"kernel": "sparse_mla_kernel<576,512,4>", "bound": "mfma", "achieved": attn_tflops,
+        roof = {"kernel": kname, "bound": "mfma", "achieved": attn_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16"}
     else:
-        roof = {"kernel": "topk_kernel", "bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
+        roof = {"kernel": kname, "bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from profiles/, or null
+    roof["traffic"] = profiled_traffic(dom, wl.name)
     roof["launches"] = launches
+    roof["avg_launch_us"] = stages[dom] * 1e3 / max(launches, 1)
     del d
     torch.cuda.empty_cache()
 
