@@ -4,32 +4,40 @@
 // the cutoff are legitimate, Sec. 5.2 near Eq. (18) -- here they go to the
 // lower index).
 //
-// One workgroup per row.  Scores are mapped to order-preserving 32-bit keys
-// (NaN lowest, -0 == +0) and the m-th largest key tau is found by a radix
-// select with 11/11/10-bit digits:
-//   pass 1 (HBM): LDS histogram of the top 11 bits -> bin b1 holding tau;
-//   pass 2 (HBM or cache): keys above bin b1 are marked in an LDS bitmap,
-//          keys inside bin b1 are compacted into an LDS candidate list;
+// One workgroup of 1024 threads per row.  Scores are mapped to
+// order-preserving 32-bit keys (NaN lowest, -0 == +0) and the m-th largest
+// key tau is found by a radix select with 13/10/9-bit digits:
+//   pass 1 (memory): LDS histogram of the top 13 bits (sign, exponent and 4
+//          mantissa bits) -> bin b1 holding tau;
+//   pass 2 (memory, mostly the Infinity Cache): keys above bin b1 are marked
+//          in an LDS bitmap, keys inside bin b1 are appended (one atomic per
+//          wave) to an LDS candidate list;
 //   digits 2 and 3 are resolved on the candidates in LDS.
-// (If bin b1 holds more keys than the candidate list can, digits 2 and 3
-// take two more passes over the row instead.)  Keys above tau go into the
-// bitmap, keys equal to tau into a tie bitmap; the first (m - #above) ties
-// in index order are kept and the bitmap is emitted in ascending order with
-// a block-wide popcount prefix sum.  The row is read at most twice in the
-// common case; the selection needs no sort.
+// If bin b1 holds more keys than the candidate list can, digits 2 and 3 take
+// two more passes over the row instead.  Keys above tau go into the bitmap,
+// keys equal to tau into a tie bitmap; the first (m - #above) ties in index
+// order are kept and the bitmap is emitted in ascending order with a
+// block-wide popcount prefix sum.  The selection needs no sort.
+//
+// The row is streamed with 16-byte loads, four per thread in flight (64 KB
+// per workgroup), after a scalar head that reaches 16-byte alignment.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kCandCap = 4096;
 constexpr int kMaxKV = 262144;
-constexpr int kBins1 = 2048;   // bits 31..21
-constexpr int kBins2 = 2048;   // bits 20..10
-constexpr int kBins3 = 1024;   // bits 9..0
+constexpr int kShift1 = 19;                 // digit 1 = key bits 31..19
+constexpr int kBins1 = 1 << (32 - kShift1); // 8192
+constexpr int kShift2 = 9;                  // digit 2 = key bits 18..9
+constexpr int kBins2 = 1 << (kShift1 - kShift2);   // 1024
+constexpr int kBins3 = 1 << kShift2;        // digit 3 = key bits 8..0: 512
+constexpr int kMaxCand = 8192;
+constexpr int kDynLds = 163840 - 1024;      // dynamic LDS bytes (the rest: static)
+constexpr int kUnroll = 4;                  // 16-byte loads in flight per thread
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -61,16 +69,19 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh)
 }
 
 // Find bin b with (count of keys in bins > b) < rank <= (count in bins >= b),
-// scanning from the top bin.  rank is 1-based.  Result in sh.bin / sh.above.
+// scanning from the top bin.  rank is 1-based and at most the total count.
+// Thread t owns bins top_t, top_t - 1, ... (per of them); the scan in thread
+// order is then a scan from the top bin down.  Result in sh.bin / sh.above.
 __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t rank, Shared& sh) {
-  const int per = nbins / kThreads;
+  const int per = (nbins + kThreads - 1) / kThreads;
   const int top = nbins - 1 - (int)threadIdx.x * per;
   uint32_t local = 0;
-  for (int j = 0; j < per; ++j) local += hist[top - j];
+  for (int j = 0; j < per; ++j)
+    if (top - j >= 0) local += hist[top - j];
   const uint32_t excl = block_exclusive_scan(local, sh);
-  if (excl < rank && rank <= excl + local) {
+  if (local > 0 && excl < rank && rank <= excl + local) {
     uint32_t cum = excl;
-    for (int j = 0; j < per; ++j) {
+    for (int j = 0; j < per && top - j >= 0; ++j) {
       const uint32_t c = hist[top - j];
       if (cum + c >= rank) { sh.bin = (uint32_t)(top - j); sh.above = cum; break; }
       cum += c;
@@ -88,7 +99,71 @@ __device__ __forceinline__ uint32_t keep_lowest(uint32_t w, uint32_t keep) {
   return r;
 }
 
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
+// Append (key, e) for the lanes with c set: one LDS atomic per wave.  Must be
+// reached by whole waves (wave-uniform control flow).
+__device__ __forceinline__ void append_wave(bool c, uint32_t key, uint32_t e, uint32_t* ckey, uint32_t* cidx,
+                                            int cap, Shared& sh) {
+  const uint64_t m = __ballot(c);
+  if (m == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(m));
+  base = __shfl(base, leader, 64);
+  if (c) {
+    const uint64_t below = lane == 0 ? 0ull : (m & (~0ull >> (64 - lane)));
+    const uint32_t pos = base + (uint32_t)__popcll(below);
+    if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = e; }
+  }
+}
+
+// The row split for vector loads: elements [0, h) are read one by one
+// (h < 4 reaches 16-byte alignment), then nq float4s, then a tail of < 4.
+struct RowSplit {
+  const float* x;
+  const float4* xv;
+  int n, h, nq, tail0;
+  __device__ __forceinline__ RowSplit(const float* p, int n_) : x(p), n(n_) {
+    const int mis = (int)(((uintptr_t)p >> 2) & 3);
+    h = min(n, (4 - mis) & 3);
+    nq = (n - h) >> 2;
+    tail0 = h + 4 * nq;
+    xv = (const float4*)(p + h);
+  }
+};
+
+// Calls f(e, key, valid) for every element of the row.  The vector part runs
+// the same number of iterations in every thread (block-uniform), so f may
+// use wave-wide operations; elements past the end come with valid = false.
+// The < 8 head and tail elements are visited by threads 0..7 afterwards with
+// a per-thread (not wave-uniform) call g(e, key).
+template <class F, class G>
+__device__ __forceinline__ void scan_row(const RowSplit& r, F&& f, G&& g) {
+  const int t = threadIdx.x;
+  const int iters = (r.nq + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  for (int it = 0; it < iters; ++it) {
+    float4 v[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = (it * kUnroll + u) * kThreads + t;
+      ok[u] = q < r.nq;
+      v[u] = r.xv[ok[u] ? q : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = r.h + 4 * ((it * kUnroll + u) * kThreads + t);
+      f(e + 0, order_key(v[u].x), ok[u]);
+      f(e + 1, order_key(v[u].y), ok[u]);
+      f(e + 2, order_key(v[u].z), ok[u]);
+      f(e + 3, order_key(v[u].w), ok[u]);
+    }
+  }
+  if (t < r.h) g(t, order_key(r.x[t]));
+  if (t >= 4 && t - 4 < r.n - r.tail0) g(r.tail0 + t - 4, order_key(r.x[r.tail0 + t - 4]));
+}
+
+__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
   extern __shared__ uint32_t lds[];
   __shared__ Shared sh;
   const int t = threadIdx.x;
@@ -101,13 +176,14 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
     for (int j = t; j < a.k; j += kThreads) out[j] = j < n ? j : -1;
     return;
   }
-  const float* x = a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld;
+  const RowSplit row(a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld, n);
   const int nwords = (n + 31) >> 5;
-  uint32_t* hist = lds;                          // kBins1 (reused for digits 2, 3)
-  uint32_t* selbm = hist + kBins1;               // nwords
-  uint32_t* tiebm = selbm + ((a.S + 31) >> 5);   // nwords
-  uint32_t* ckey = tiebm + ((a.S + 31) >> 5);    // kCandCap
-  uint32_t* cidx = ckey + kCandCap;              // kCandCap
+  const int words_max = (a.S + 31) >> 5;
+  uint32_t* hist = lds;                  // kBins1 (reused for digits 2, 3)
+  uint32_t* selbm = hist + kBins1;       // nwords
+  uint32_t* tiebm = selbm + words_max;   // nwords
+  uint32_t* ckey = tiebm + words_max;    // cap
+  uint32_t* cidx = ckey + cap;           // cap
 
   for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
   for (int j = t; j < nwords; j += kThreads) { selbm[j] = 0; tiebm[j] = 0; }
@@ -115,14 +191,9 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   __syncthreads();
 
   // ---- pass 1: digit-1 histogram
-  for (int e0 = t; e0 < n; e0 += 4 * kThreads) {
-    float v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) { const int e = e0 + u * kThreads; v[u] = e < n ? x[e] : 0.f; }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (e0 + u * kThreads < n) atomicAdd(&hist[order_key(v[u]) >> 21], 1u);
-  }
+  scan_row(
+      row, [&](int, uint32_t key, bool ok) { if (ok) atomicAdd(&hist[key >> kShift1], 1u); },
+      [&](int, uint32_t key) { atomicAdd(&hist[key >> kShift1], 1u); });
   __syncthreads();
   find_bin(hist, kBins1, (uint32_t)m, sh);
   const uint32_t b1 = sh.bin;
@@ -131,27 +202,27 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   __syncthreads();
 
   uint32_t tau, need;
-  if (c1 <= kCandCap) {
+  if (c1 <= (uint32_t)cap) {
     // ---- pass 2: mark keys above bin b1, collect bin b1
-    for (int e0 = t; e0 < n; e0 += 4 * kThreads) {
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { const int e = e0 + u * kThreads; v[u] = e < n ? x[e] : 0.f; }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kThreads;
-        if (e < n) {
-          const uint32_t key = order_key(v[u]);
-          const uint32_t d = key >> 21;
+    scan_row(
+        row,
+        [&](int e, uint32_t key, bool ok) {
+          const uint32_t d = key >> kShift1;
+          if (ok && d > b1) set_bit(selbm, e);
+          append_wave(ok && d == b1, key, (uint32_t)e, ckey, cidx, cap, sh);
+        },
+        [&](int e, uint32_t key) {
+          const uint32_t d = key >> kShift1;
           if (d > b1) set_bit(selbm, e);
-          else if (d == b1) { const uint32_t pos = atomicAdd(&sh.ncand, 1u); ckey[pos] = key; cidx[pos] = (uint32_t)e; }
-        }
-      }
-    }
+          else if (d == b1) {
+            const uint32_t pos = atomicAdd(&sh.ncand, 1u);
+            if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
+          }
+        });
     for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
     __syncthreads();
-    const int nc = (int)sh.ncand;
-    for (int c = t; c < nc; c += kThreads) atomicAdd(&hist[(ckey[c] >> 10) & 0x7FFu], 1u);
+    const int nc = (int)min(sh.ncand, (uint32_t)cap);   // == c1
+    for (int c = t; c < nc; c += kThreads) atomicAdd(&hist[(ckey[c] >> kShift2) & (kBins2 - 1)], 1u);
     __syncthreads();
     find_bin(hist, kBins2, rank1, sh);
     const uint32_t b2 = sh.bin;
@@ -160,10 +231,10 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
     for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
     __syncthreads();
     for (int c = t; c < nc; c += kThreads)
-      if (((ckey[c] >> 10) & 0x7FFu) == b2) atomicAdd(&hist[ckey[c] & 0x3FFu], 1u);
+      if (((ckey[c] >> kShift2) & (kBins2 - 1)) == b2) atomicAdd(&hist[ckey[c] & (kBins3 - 1)], 1u);
     __syncthreads();
     find_bin(hist, kBins3, rank2, sh);
-    tau = (b1 << 21) | (b2 << 10) | sh.bin;
+    tau = (b1 << kShift1) | (b2 << kShift2) | sh.bin;
     need = rank2 - sh.above;
     for (int c = t; c < nc; c += kThreads) {
       const uint32_t key = ckey[c];
@@ -174,30 +245,30 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
     // ---- wide bin: resolve digits 2 and 3 with extra passes over the row
     for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
     __syncthreads();
-    for (int e = t; e < n; e += kThreads) {
-      const uint32_t key = order_key(x[e]);
-      if ((key >> 21) == b1) atomicAdd(&hist[(key >> 10) & 0x7FFu], 1u);
-    }
+    auto h2 = [&](int, uint32_t key) {
+      if ((key >> kShift1) == b1) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
+    };
+    scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h2(e, key); }, h2);
     __syncthreads();
     find_bin(hist, kBins2, rank1, sh);
-    const uint32_t pre = (b1 << 11) | sh.bin;
+    const uint32_t pre = (b1 << (kShift1 - kShift2)) | sh.bin;
     const uint32_t rank2 = rank1 - sh.above;
     __syncthreads();
     for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
     __syncthreads();
-    for (int e = t; e < n; e += kThreads) {
-      const uint32_t key = order_key(x[e]);
-      if ((key >> 10) == pre) atomicAdd(&hist[key & 0x3FFu], 1u);
-    }
+    auto h3 = [&](int, uint32_t key) {
+      if ((key >> kShift2) == pre) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+    };
+    scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h3(e, key); }, h3);
     __syncthreads();
     find_bin(hist, kBins3, rank2, sh);
-    tau = (pre << 10) | sh.bin;
+    tau = (pre << kShift2) | sh.bin;
     need = rank2 - sh.above;
-    for (int e = t; e < n; e += kThreads) {
-      const uint32_t key = order_key(x[e]);
+    auto mark = [&](int e, uint32_t key) {
       if (key > tau) set_bit(selbm, e);
       else if (key == tau) set_bit(tiebm, e);
-    }
+    };
+    scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) mark(e, key); }, mark);
   }
   __syncthreads();
 
@@ -238,16 +309,19 @@ int topk_max_kv() { return kMaxKV; }
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.rows <= 0 || a.B <= 0) return hipSuccess;
   const size_t words = (size_t)((a.S + 31) >> 5);
-  const size_t lds = (kBins1 + 2 * words + 2 * kCandCap) * sizeof(uint32_t);
+  const size_t fixed = (kBins1 + 2 * words) * sizeof(uint32_t);
+  // Candidate capacity: what the LDS budget leaves, at most kMaxCand (at the
+  // largest supported S this is still ~7900, above any plausible cutoff bin).
+  const int cap = (int)min((size_t)kMaxCand, (kDynLds - fixed) / (2 * sizeof(uint32_t)));
+  const size_t lds = fixed + 2 * (size_t)cap * sizeof(uint32_t);
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t max_lds = (kBins1 + 2 * (size_t)(kMaxKV / 32) + 2 * kCandCap) * sizeof(uint32_t);
-    const hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)max_lds);
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a, cap);
   return hipGetLastError();
 }
 
