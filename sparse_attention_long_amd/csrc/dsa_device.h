@@ -84,4 +84,37 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS DMA (global_load_lds) issued from inline asm: each lane copies 16
+// (or 4) bytes from `src` to lds_base + 16*lane (4*lane); lds_base must be
+// wave-uniform.  The compiler's wait insertion cannot tell separate LDS
+// buffers apart: it would make every LDS read wait for all DMA in flight,
+// including prefetches into other buffers.  Copies issued here are invisible
+// to it, so the kernels await completion explicitly (wait_dma / a counted
+// s_waitcnt vmcnt) before the barrier that publishes a buffer.  M0 is saved
+// and restored around the copy.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+__device__ __forceinline__ void dma_x4(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma_x1(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
+}
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the "saddr" form): one VGPR of address per lane.  No memory
+// clobber: the caller guarantees that nothing reads or writes the target
+// buffer between this copy and the barrier that publishes it (volatile asm
+// statements keep their order, so the copy stays between its barriers).
+__device__ __forceinline__ void dma_x4_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_base));
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace dsa

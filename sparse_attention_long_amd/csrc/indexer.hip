@@ -231,28 +231,6 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
 // waves per workgroup lets two workgroups share a CU, so one's barrier
 // waits and prologue are covered by the other's work.
 //
-// LDS DMA (global_load_lds) issued from inline asm: each lane copies 16
-// (or 4) bytes from `src` to lds_base + 16*lane (4*lane).  The compiler's
-// wait insertion cannot tell the two staging buffers apart and would make
-// every LDS read wait for all DMA in flight (including the prefetch into
-// the other buffer), so the copies are hidden from it and completion is
-// awaited explicitly with wait_dma() before the barrier that publishes a
-// buffer.  M0 is saved and restored around the copy.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-__device__ __forceinline__ void dma_x4(const void* src, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
-}
-__device__ __forceinline__ void dma_x1(const void* src, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
-}
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 constexpr int kSubKeys = 256;
 constexpr int kSubBytes = kSubKeys * 128;
 constexpr int kLdsWaves = 4;

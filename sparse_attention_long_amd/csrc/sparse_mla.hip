@@ -79,49 +79,63 @@ __device__ __forceinline__ int piece_pos(int r, int p) {
   return (C::kBaseB + r * C::kPB + (pb ^ (r & (C::kPB - 1)))) * 8;
 }
 
-// Gather one chunk's rows into a tile with global_load_lds_dwordx4: each
-// wave instruction fills 64 consecutive 16-byte LDS pieces, lane l filling
-// piece base + l from the global row piece that belongs there.  Instruction
-// j goes to wave j % NW, so every wave issues kDma / NW instructions.  An
+// Gather one chunk's rows into a tile with global_load_lds_dwordx4 (issued
+// from inline asm, see dma_x4): each wave instruction fills 64 consecutive
+// 16-byte LDS pieces, lane l filling piece base + l from the global row
+// piece that belongs there.  Instruction j goes to wave j % NW, so every
+// wave issues kDma / NW instructions; issue(jj) sends this wave's jj-th.  An
 // invalid row index reads row 0 (finite data, masked out of the softmax).
-// `row_of_lane`: lane j < 32 holds the chunk's j-th row index.
+// Set-up computes the chunk's row addresses once (one 64-bit product per
+// lane); each row copy then needs two lane reads into SGPRs, one offset
+// VGPR and the M0 set-up.
 template <int DK, int DV, int NW>
-__device__ __forceinline__ void gather_dma(uint16_t* tile, const uint16_t* kvb, int row_of_lane) {
+struct ChunkGather {
   using C = Cfg<DK, DV, NW>;
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));   // recompute the cheap per-lane offsets here, do not hoist them
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int jj = 0; jj < C::kDma / NW; ++jj) {
-    const int j = jj * NW + wave;                 // wave-uniform instruction index
+  uint16_t* tile;
+  const uint16_t* kvb;
+  int row_of_lane;    // lane j < 32 holds the chunk's j-th row index (or < 0)
+  uint32_t addr_lo, addr_hi;   // lane j < 32: byte address of that row
+  int wave;
+
+  __device__ __forceinline__ void init(uint16_t* t, const uint16_t* kv, int rol) {
+    tile = t;
+    kvb = kv;
+    row_of_lane = max(rol, 0);
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t ad = (uint64_t)(uintptr_t)(kvb + (int64_t)row_of_lane * DK);
+    addr_lo = (uint32_t)ad;
+    addr_hi = (uint32_t)(ad >> 32);
+  }
+  __device__ __forceinline__ void issue(int jj) const {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));   // keep the cheap per-lane offsets here, do not hoist them
+    const int j = jj * NW + wave;   // wave-uniform instruction index
     // Whether instruction jj of every wave lies in part A or part B is known
     // at compile time for the shapes built here (no wave straddles).
     const bool in_a = (jj + 1) * NW <= C::kDmaA ? true : (jj * NW >= C::kDmaA ? false : j < C::kDmaA);
-    const uint16_t* src;
-    uint16_t* dst;
     if (C::kRowDma && in_a) {
       // one row per instruction: scalar row base + per-lane swizzled piece
-      const int s = max(__builtin_amdgcn_readlane(row_of_lane, j), 0);
-      const uint16_t* rowp = kvb + (int64_t)s * DK;
-      src = rowp + 8 * (lane ^ swz_a(j));
-      dst = tile + j * C::kRA * 8;
+      const uint64_t rowp = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, j) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)addr_lo, j);
+      dma_x4_s(16u * (uint32_t)(lane ^ swz_a(j)), (const void*)(uintptr_t)rowp, lds_addr(tile + j * C::kRA * 8));
     } else if (in_a) {
       const int q = j * kWave + lane;             // piece of the contiguous part A
       const int r = q / C::kPA, pp = q % C::kPA;
-      const int s = max(__shfl(row_of_lane, r, kWave), 0);
-      src = kvb + (int64_t)s * DK + 8 * (pp ^ swz_a(r));
-      dst = tile + j * kWave * 8;
+      const int s = __shfl(row_of_lane, r, kWave);
+      dma_x4(kvb + (int64_t)s * DK + 8 * (pp ^ swz_a(r)), lds_addr(tile + j * kWave * 8));
     } else {
       const int q = (j - C::kDmaA) * kWave + lane;  // piece of part B
       const int r = q / C::kPB, pp = q % C::kPB;
-      const int s = max(__shfl(row_of_lane, r, kWave), 0);
-      src = kvb + (int64_t)s * DK + 8 * (C::kPA + (pp ^ (r & (C::kPB - 1))));
-      dst = tile + (C::kBaseB + (j - C::kDmaA) * kWave) * 8;
+      const int s = __shfl(row_of_lane, r, kWave);
+      dma_x4(kvb + (int64_t)s * DK + 8 * (C::kPA + (pp ^ (r & (C::kPB - 1)))),
+             lds_addr(tile + (C::kBaseB + (j - C::kDmaA) * kWave) * 8));
     }
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   }
-}
+  __device__ __forceinline__ void issue_all() const {
+#pragma unroll
+    for (int jj = 0; jj < C::kDma / NW; ++jj) issue(jj);
+  }
+};
 
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -285,13 +299,17 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   // tile); before that barrier each wave waits until its own part of chunk c
   // has landed while chunk c+1's DMA stays in flight.
   auto step = [&](int c, const uint16_t* cur, uint16_t* fill) {
+    // Each wave waits until its own copies of chunk c landed (chunk c+1's
+    // stay in flight); the barrier then publishes the tile.  A compiler-level
+    // memory barrier keeps LDS accesses on their side of it; the tile
+    // refilled next was last read (and consumed) in chunk c-1.
     if (c + 1 < nchunks) wait_vm<ndma>(); else wait_vm<0>();
-    // A bare barrier: __syncthreads() would add a release fence that waits
-    // for every outstanding DMA, including the chunks being prefetched.
-    // Chunk c's tile is complete once every wave passed its wait above, and
-    // the tile refilled next was last read (and consumed) in chunk c-1.
-    __builtin_amdgcn_s_barrier();
-    if (c + 2 < nchunks) gather_dma<DK, DV, NW>(fill, kvb, sidx[(c + 2) * kChunk + (lane & 31)]);
+    asm volatile("s_barrier" ::: "memory");
+    if (c + 2 < nchunks) {
+      ChunkGather<DK, DV, NW> g;
+      g.init(fill, kvb, sidx[(c + 2) * kChunk + (lane & 31)]);
+      g.issue_all();
+    }
     const uint32_t valid =
         (uint32_t)__builtin_amdgcn_ballot_w64(lane < kChunk && sidx[c * kChunk + (lane & 31)] >= 0);
     if (valid != 0u) attend_chunk<DK, DV, NW>(cur, valid, qb, zscale, rs);
@@ -301,8 +319,11 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < C::kNT; ++t) rs.o[t] = (v16f){};
     rs.l_sum = 0.f;
-    if (nchunks > 0) gather_dma<DK, DV, NW>(tile0, kvb, sidx[lane & 31]);
-    if (nchunks > 1) gather_dma<DK, DV, NW>(tile1, kvb, sidx[kChunk + (lane & 31)]);
+    {
+      ChunkGather<DK, DV, NW> g;
+      if (nchunks > 0) { g.init(tile0, kvb, sidx[lane & 31]); g.issue_all(); }
+      if (nchunks > 1) { g.init(tile1, kvb, sidx[kChunk + (lane & 31)]); g.issue_all(); }
+    }
     for (int c = 0; c < nchunks; c += 3) {
       step(c, tile0, tile2);
       if (c + 1 >= nchunks) break;
@@ -311,6 +332,7 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
       step(c + 2, tile2, tile1);
     }
     // A logit far above its head's reference: redo the row with the true max.
+    wait_dma();
     if (threadIdx.x == 0) redo = 0;
     __syncthreads();
     if (rs.m_seen > rs.m_ref + kRefHeadroom) redo = 1;
