@@ -117,6 +117,21 @@ __device__ __forceinline__ void append_wave(bool c, uint32_t key, uint32_t e, ui
   }
 }
 
+// Exclusive prefix over the wave of per-lane counts below 32, and the
+// wave total, from five ballots (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_prefix_small(uint32_t cnt, uint32_t& total) {
+  uint32_t pre = 0;
+  total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t bm = __ballot((cnt >> bit) & 1u);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+    pre += below << bit;
+    total += (uint32_t)__popcll(bm) << bit;
+  }
+  return pre;
+}
+
 // The row split for vector loads: elements [0, h) are read one by one
 // (h < 4 reaches 16-byte alignment), then nq float4s, then a tail of < 4.
 struct RowSplit {
@@ -190,85 +205,182 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
   if (t == 0) sh.ncand = 0;
   __syncthreads();
 
-  // ---- pass 1: digit-1 histogram
-  scan_row(
-      row, [&](int, uint32_t key, bool ok) { if (ok) atomicAdd(&hist[key >> kShift1], 1u); },
-      [&](int, uint32_t key) { atomicAdd(&hist[key >> kShift1], 1u); });
-  __syncthreads();
-  find_bin(hist, kBins1, (uint32_t)m, sh);
-  const uint32_t b1 = sh.bin;
-  const uint32_t rank1 = (uint32_t)m - sh.above;   // rank of tau inside bin b1
-  const uint32_t c1 = hist[b1];
-  __syncthreads();
-
+  // Digits 2 and 3 of tau among the candidate list (every key of bin b1 is
+  // on it; keys of other bins are filtered out), then the marks: keys above
+  // tau into the bitmap, keys equal to tau into the tie bitmap.
   uint32_t tau, need;
-  if (c1 <= (uint32_t)cap) {
-    // ---- pass 2: mark keys above bin b1, collect bin b1
-    scan_row(
-        row,
-        [&](int e, uint32_t key, bool ok) {
-          const uint32_t d = key >> kShift1;
-          if (ok && d > b1) set_bit(selbm, e);
-          append_wave(ok && d == b1, key, (uint32_t)e, ckey, cidx, cap, sh);
-        },
-        [&](int e, uint32_t key) {
-          const uint32_t d = key >> kShift1;
-          if (d > b1) set_bit(selbm, e);
-          else if (d == b1) {
-            const uint32_t pos = atomicAdd(&sh.ncand, 1u);
-            if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
-          }
-        });
+  auto select_candidates = [&](int nc, uint32_t b1, uint32_t rank1) {
     for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
     __syncthreads();
-    const int nc = (int)min(sh.ncand, (uint32_t)cap);   // == c1
-    for (int c = t; c < nc; c += kThreads) atomicAdd(&hist[(ckey[c] >> kShift2) & (kBins2 - 1)], 1u);
+    for (int c = t; c < nc; c += kThreads)
+      if ((ckey[c] >> kShift1) == b1) atomicAdd(&hist[(ckey[c] >> kShift2) & (kBins2 - 1)], 1u);
     __syncthreads();
     find_bin(hist, kBins2, rank1, sh);
-    const uint32_t b2 = sh.bin;
+    const uint32_t pre = (b1 << (kShift1 - kShift2)) | sh.bin;
     const uint32_t rank2 = rank1 - sh.above;
-    __syncthreads();
     for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
     __syncthreads();
     for (int c = t; c < nc; c += kThreads)
-      if (((ckey[c] >> kShift2) & (kBins2 - 1)) == b2) atomicAdd(&hist[ckey[c] & (kBins3 - 1)], 1u);
+      if ((ckey[c] >> kShift2) == pre) atomicAdd(&hist[ckey[c] & (kBins3 - 1)], 1u);
     __syncthreads();
     find_bin(hist, kBins3, rank2, sh);
-    tau = (b1 << kShift1) | (b2 << kShift2) | sh.bin;
+    tau = (pre << kShift2) | sh.bin;
     need = rank2 - sh.above;
     for (int c = t; c < nc; c += kThreads) {
       const uint32_t key = ckey[c];
       if (key > tau) set_bit(selbm, (int)cidx[c]);
       else if (key == tau) set_bit(tiebm, (int)cidx[c]);
     }
-  } else {
-    // ---- wide bin: resolve digits 2 and 3 with extra passes over the row
-    for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
+  };
+
+  // ---- one pass with a sampled cutoff: 32 blocks of 64 scores spread over
+  // the row give a conservative lower bound lo for tau (the sample's rank-r
+  // bin, r chosen so that about 2m keys are expected at or above it); the
+  // row is then read once and every key >= lo is collected.  If between m
+  // and cap keys were collected, tau is the m-th largest candidate and the
+  // selection is exact; otherwise the two-pass radix select below runs.
+  bool done = false;
+  {
+    const int blk = t >> 5;
+    const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + 2 * (t & 31);
+    atomicAdd(&hist[order_key(row.x[e0]) >> kShift1], 1u);
+    atomicAdd(&hist[order_key(row.x[e0 + 1]) >> kShift1], 1u);
     __syncthreads();
-    auto h2 = [&](int, uint32_t key) {
-      if ((key >> kShift1) == b1) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
-    };
-    scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h2(e, key); }, h2);
+    const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
+    find_bin(hist, kBins1, r, sh);
+    const uint32_t lo = sh.bin << kShift1;
+    for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
+    {
+      // One wave-level append per iteration: each lane marks its candidates
+      // among its 4 x 4 scores, the wave forms the prefix of the counts from
+      // ballots, and one LDS atomic reserves the wave's slots.
+      const int lane = t & 63;
+      const int iters = (row.nq + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+      for (int it = 0; it < iters; ++it) {
+        float4 v[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int q = (it * kUnroll + u) * kThreads + t;
+          ok[u] = q < row.nq;
+          v[u] = row.xv[ok[u] ? q : 0];
+        }
+        uint32_t keys[4 * kUnroll];
+        uint32_t cm = 0;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          keys[4 * u + 0] = order_key(v[u].x);
+          keys[4 * u + 1] = order_key(v[u].y);
+          keys[4 * u + 2] = order_key(v[u].z);
+          keys[4 * u + 3] = order_key(v[u].w);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) cm |= (ok[u] && keys[4 * u + c] >= lo ? 1u : 0u) << (4 * u + c);
+        }
+        uint32_t total;
+        const uint32_t pre = wave_prefix_small((uint32_t)__popc(cm), total);
+        if (total != 0) {   // wave-uniform
+          const int leader = 0;
+          uint32_t base = 0;
+          if (lane == leader) base = atomicAdd(&sh.ncand, total);
+          base = __shfl(base, leader, 64);
+          uint32_t pos = base + pre;
+#pragma unroll
+          for (int j = 0; j < 4 * kUnroll; ++j) {
+            if ((cm >> j) & 1u) {
+              if (pos < (uint32_t)cap) {
+                ckey[pos] = keys[j];
+                cidx[pos] = (uint32_t)(row.h + 4 * ((it * kUnroll + (j >> 2)) * kThreads + t) + (j & 3));
+              }
+              ++pos;
+            }
+          }
+        }
+      }
+      auto tail = [&](int e) {
+        const uint32_t key = order_key(row.x[e]);
+        if (key >= lo) {
+          const uint32_t pos = atomicAdd(&sh.ncand, 1u);
+          if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
+        }
+      };
+      if (t < row.h) tail(t);
+      if (t >= 4 && t - 4 < row.n - row.tail0) tail(row.tail0 + t - 4);
+    }
     __syncthreads();
-    find_bin(hist, kBins2, rank1, sh);
-    const uint32_t pre = (b1 << (kShift1 - kShift2)) | sh.bin;
-    const uint32_t rank2 = rank1 - sh.above;
+    const uint32_t nc = sh.ncand;
+    if (nc >= (uint32_t)m && nc <= (uint32_t)cap) {   // block-uniform
+      for (int c = t; c < (int)nc; c += kThreads) atomicAdd(&hist[ckey[c] >> kShift1], 1u);
+      __syncthreads();
+      find_bin(hist, kBins1, (uint32_t)m, sh);
+      const uint32_t b1 = sh.bin;
+      const uint32_t rank1 = (uint32_t)m - sh.above;
+      select_candidates((int)nc, b1, rank1);
+      done = true;
+    } else {
+      if (t == 0) sh.ncand = 0;
+      __syncthreads();
+    }
+  }
+
+  if (!done) {
+    // ---- pass 1: digit-1 histogram
+    scan_row(
+        row, [&](int, uint32_t key, bool ok) { if (ok) atomicAdd(&hist[key >> kShift1], 1u); },
+        [&](int, uint32_t key) { atomicAdd(&hist[key >> kShift1], 1u); });
     __syncthreads();
-    for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
+    find_bin(hist, kBins1, (uint32_t)m, sh);
+    const uint32_t b1 = sh.bin;
+    const uint32_t rank1 = (uint32_t)m - sh.above;   // rank of tau inside bin b1
+    const uint32_t c1 = hist[b1];
     __syncthreads();
-    auto h3 = [&](int, uint32_t key) {
-      if ((key >> kShift2) == pre) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
-    };
-    scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h3(e, key); }, h3);
-    __syncthreads();
-    find_bin(hist, kBins3, rank2, sh);
-    tau = (pre << kShift2) | sh.bin;
-    need = rank2 - sh.above;
-    auto mark = [&](int e, uint32_t key) {
-      if (key > tau) set_bit(selbm, e);
-      else if (key == tau) set_bit(tiebm, e);
-    };
-    scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) mark(e, key); }, mark);
+    if (c1 <= (uint32_t)cap) {
+      // ---- pass 2: mark keys above bin b1, collect bin b1
+      scan_row(
+          row,
+          [&](int e, uint32_t key, bool ok) {
+            const uint32_t d = key >> kShift1;
+            if (ok && d > b1) set_bit(selbm, e);
+            append_wave(ok && d == b1, key, (uint32_t)e, ckey, cidx, cap, sh);
+          },
+          [&](int e, uint32_t key) {
+            const uint32_t d = key >> kShift1;
+            if (d > b1) set_bit(selbm, e);
+            else if (d == b1) {
+              const uint32_t pos = atomicAdd(&sh.ncand, 1u);
+              if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
+            }
+          });
+      __syncthreads();
+      select_candidates((int)min(sh.ncand, (uint32_t)cap), b1, rank1);   // == c1 candidates
+    } else {
+      // ---- wide bin: resolve digits 2 and 3 with extra passes over the row
+      for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
+      __syncthreads();
+      auto h2 = [&](int, uint32_t key) {
+        if ((key >> kShift1) == b1) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
+      };
+      scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h2(e, key); }, h2);
+      __syncthreads();
+      find_bin(hist, kBins2, rank1, sh);
+      const uint32_t pre = (b1 << (kShift1 - kShift2)) | sh.bin;
+      const uint32_t rank2 = rank1 - sh.above;
+      __syncthreads();
+      for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
+      __syncthreads();
+      auto h3 = [&](int, uint32_t key) {
+        if ((key >> kShift2) == pre) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+      };
+      scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h3(e, key); }, h3);
+      __syncthreads();
+      find_bin(hist, kBins3, rank2, sh);
+      tau = (pre << kShift2) | sh.bin;
+      need = rank2 - sh.above;
+      auto mark = [&](int e, uint32_t key) {
+        if (key > tau) set_bit(selbm, e);
+        else if (key == tau) set_bit(tiebm, e);
+      };
+      scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) mark(e, key); }, mark);
+    }
   }
   __syncthreads();
 
