@@ -163,6 +163,41 @@ def profiled_traffic(stage, workload):
     return float(vals["traffic_bytes_per_launch"])
 
 
+def time_quantize(torch, dsa, wl, stream, reps=5):
+    """Per-token FP8 quantisation of the workload's index keys (f32, [S, d_I])
+    and of 16384 query tokens (bf16, [16384, H_I * d_I]): HBM-bound, reported
+    as algorithmic GB/s (values read + codes and scales written)."""
+    from synth import gen
+    from synth.device import lib as synth_lib, _check
+    L = synth_lib()
+    S, dI, tq = wl.n_kv, wl.idx_dim, 16384
+    ql = wl.idx_heads * wl.idx_dim
+    kx = torch.empty((S, dI), dtype=torch.float32, device="cuda")
+    qx = torch.empty((tq, ql), dtype=torch.int16, device="cuda")
+    _check(L.synth_fill_f32(wl.seed, gen.TID["k_idx"], 0, S * dI, 0, kx.data_ptr(), stream.cuda_stream))
+    _check(L.synth_fill_bf16(wl.seed, gen.TID["q_idx"], 0, tq * ql, 0, qx.data_ptr(), stream.cuda_stream))
+    kc = torch.empty((S, dI), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((S,), dtype=torch.float32, device="cuda")
+    qc = torch.empty((tq, ql), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((tq,), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, x, n, ln, c, sc, dt, eb in (("index_keys_f32", kx, S, dI, kc, ks, 0, 4), ("queries_bf16", qx, tq, ql, qc, qs, 1, 2)):
+        dsa.dsa.dsa_quantize_e4m3(x, n, ln, c, sc, dtype=dt, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        t = Timer(torch, stream)
+        e0 = t.event()
+        for _ in range(reps):
+            dsa.dsa.dsa_quantize_e4m3(x, n, ln, c, sc, dtype=dt, stream=stream.cuda_stream)
+        e1 = t.event()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = n * ln * (eb + 1) + 4 * n
+        res[name] = {"tokens": n, "token_len": ln, "us": ms * 1e3, "GB_per_s": nbytes / (ms / 1e3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    del kx, qx, kc, ks, qc, qs
+    return res
+
+
 def cpu_baseline(wl, n_rows):
     """The CPU oracle (unchanged) on a stratified sample of query rows:
     rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
@@ -287,6 +322,13 @@ def main():
         del dd
         torch.cuda.empty_cache()
 
+    quant = None
+    if not args.no_decode:
+        log("[bench] FP8 quantisation of the index keys and of 16384 query tokens")
+        quant = time_quantize(torch, dsa, wl, stream)
+        log(f"[bench] quantise {quant}")
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_rows} rows")
@@ -301,7 +343,7 @@ def main():
                    "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim, "heads": wl.heads, "dim_qk": wl.dim_qk,
                    "dim_v": wl.dim_v},
         "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
-        "topk_GB_per_s": topk_gbs, "roofline": roof, "decode": decode, "cpu_baseline": cpu,
+        "topk_GB_per_s": topk_gbs, "roofline": roof, "decode": decode, "quantize": quant, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 

@@ -132,6 +132,42 @@ int dsa_forward(const dsa_dims* dims, const uint8_t* q_idx, const float* q_scale
                 float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                 void* stream);
 
+/*
+ * Per-token FP8 quantisation: the step that produces the FP8 indexer inputs
+ * (the indexer runs in FP8, Sec. 1.1).  Format: OCP E4M3FN with one fp32
+ * scale per token.  For each token t (token_len values x):
+ *   scales[t]   = amax_t / 448, a correctly rounded fp32 division
+ *                 (1.0 when amax_t == 0)
+ *   codes[t, j] = e4m3(x[t, j] / scales[t]), the division correctly rounded
+ *                 in fp32 and the conversion rounding to nearest, ties to
+ *                 even, saturating at +-448 (a -0.0 quotient gives 0x80)
+ *
+ *   x       [n_tokens, token_len]  f32 (x_dtype 0) or bf16 (x_dtype 1),
+ *           finite values (non-finite input gives unspecified codes)
+ *   codes   [n_tokens, token_len]  e4m3 out
+ *   scales  [n_tokens]             f32 out
+ * token_len: a multiple of 4 in [4, 16384].  x must be 16-byte aligned for
+ * f32 and 8-byte aligned for bf16; codes 4-byte aligned.
+ */
+int dsa_quantize_e4m3(const void* x, int x_dtype, int64_t n_tokens, int32_t token_len, uint8_t* codes,
+                      float* scales, void* stream);
+
+/*
+ * Decode cache append: the n_q new tokens of every sequence, at positions
+ * q_pos0 .. q_pos0 + n_q - 1, are written into the caches the calls above
+ * read (a new token is in the cache before it attends, so with
+ * q_pos0 = n_kv - 1 the decode query sees itself):
+ *   k_new   [B, n_q, d_I]  f32 or bf16 (k_dtype 0 / 1), quantised exactly as
+ *           by dsa_quantize_e4m3 into k_idx [B, n_kv, d_I] and
+ *           k_scale [B, n_kv]
+ *   kv_new  [B, n_q, Dk]   bf16, copied into kv [B, n_kv, Dk]
+ * Other cache rows are untouched.  kv_new and kv may both be NULL to skip
+ * the latent copy.  Uses batch, n_q, n_kv, q_pos0, idx_dim and dim_qk of
+ * dims (dim_qk: a multiple of 8).
+ */
+int dsa_cache_append(const dsa_dims* dims, const void* k_new, int k_dtype, const uint16_t* kv_new,
+                     uint8_t* k_idx, float* k_scale, uint16_t* kv, void* stream);
+
 /* Status text, thread-local last error message, ABI version (major*100+minor). */
 const char* dsa_status_string(int status);
 const char* dsa_last_error(void);

@@ -79,6 +79,47 @@ def dequant_e4m3(codes, scales) -> np.ndarray:
     return v * s.reshape(s.shape + (1,) * (v.ndim - s.ndim))
 
 
+# ----------------------------------------------------------------- quantisation
+def quantize_e4m3_tokens(x):
+    """Per-token FP8 quantisation (the FP8 indexer inputs of Sec. 1.1, in the
+    format and scale granularity this build reads into the pages): scale =
+    amax / 448 in float32 (1 for an all-zero token); each value is divided by
+    the scale in float32 and rounded to the nearest E4M3FN value, ties to the
+    even code, with magnitudes of 448 and above saturating to 448.  The sign
+    of the quotient is kept (a -0.0 quotient gives code 0x80).
+
+    x: [..., token_len] values; returns (codes uint8 [..., token_len],
+    scales float32 [...])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = (x32 / scale[..., None]).astype(np.float32)
+    a = np.abs(y).astype(np.float64)
+    vals = E4M3_VALUES[:0x7F]                     # codes 0x00..0x7E, increasing, 0 .. 448
+    hi = np.clip(np.searchsorted(vals, a), 1, 0x7E)
+    lo = hi - 1
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a >= 448.0, 0x7E, code)
+    code = code.astype(np.uint8) | (np.signbit(y).astype(np.uint8) << np.uint8(7))
+    return code.astype(np.uint8), scale
+
+
+def cache_append(k_cache, k_scale_cache, kv_cache, k_new, kv_new, pos0: int):
+    """The decode cache update: the new tokens of every sequence (axis 1 of
+    k_new / kv_new) are quantised (keys) or copied (latents) into rows
+    pos0 .. pos0 + n - 1 of the caches; returns updated copies."""
+    kc, ks, kv = np.array(k_cache), np.array(k_scale_cache), None if kv_cache is None else np.array(kv_cache)
+    codes, scales = quantize_e4m3_tokens(k_new)
+    n = codes.shape[1]
+    kc[:, pos0:pos0 + n] = codes
+    ks[:, pos0:pos0 + n] = scales
+    if kv is not None:
+        kv[:, pos0:pos0 + n] = kv_new
+    return kc, ks, kv
+
+
 # ----------------------------------------------------------------- shapes
 def n_candidates(p: int, n_kv: int) -> int:
     """n_p = min(p + 1, S): inclusive causal row length at absolute position p."""

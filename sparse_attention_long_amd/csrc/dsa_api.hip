@@ -1,6 +1,7 @@
 // C ABI of the DSA forward path: argument validation, workspace planning and
 // kernel dispatch.  Every check runs on the host before the first HIP call,
 // so invalid calls leave outputs untouched and launch nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -138,7 +139,7 @@ dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const flo
 
 extern "C" {
 
-int dsa_version(void) { return 100; }
+int dsa_version(void) { return 101; }
 
 const char* dsa_status_string(int status) {
   switch (status) {
@@ -309,6 +310,55 @@ int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, c
     if (e != hipSuccess) return hip_status(e, "attention launch");
   }
   return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int dsa_quantize_e4m3(const void* x, int x_dtype, int64_t n_tokens, int32_t token_len, uint8_t* codes,
+                      float* scales, void* stream) {
+  REQUIRE(x && codes && scales, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(x_dtype == 0 || x_dtype == 1, DSA_ERR_INVALID_ARG, "x_dtype must be 0 (f32) or 1 (bf16), got %d", x_dtype);
+  REQUIRE(n_tokens >= 0 && n_tokens <= (1ll << 30), DSA_ERR_INVALID_ARG, "n_tokens out of range (%lld)",
+          (long long)n_tokens);
+  REQUIRE(token_len >= 4 && token_len <= 16384 && token_len % 4 == 0, DSA_ERR_UNSUPPORTED,
+          "token_len must be a multiple of 4 in [4, 16384] (got %d)", token_len);
+  REQUIRE(aligned(x, x_dtype == 0 ? 16 : 8) && aligned(codes, 4) && aligned(scales, 4), DSA_ERR_INVALID_ARG,
+          "misaligned x/codes/scales pointer");
+  return hip_status(dsa::launch_quantize(x, x_dtype, n_tokens, token_len, (int32_t)std::max<int64_t>(n_tokens, 1),
+                                         0, 0, codes, scales, (hipStream_t)stream),
+                    "quantize launch");
+}
+
+int dsa_cache_append(const dsa_dims* d, const void* k_new, int k_dtype, const uint16_t* kv_new, uint8_t* k_idx,
+                     float* k_scale, uint16_t* kv, void* stream) {
+  REQUIRE(d != nullptr, DSA_ERR_INVALID_ARG, "dims is NULL");
+  REQUIRE(d->batch >= 1 && d->n_q >= 1 && d->n_kv >= 1, DSA_ERR_INVALID_ARG,
+          "batch, n_q and n_kv must be >= 1 (got %d, %d, %d)", d->batch, d->n_q, d->n_kv);
+  REQUIRE(d->q_pos0 >= 0 && (int64_t)d->q_pos0 + d->n_q <= d->n_kv, DSA_ERR_INVALID_ARG,
+          "new positions q_pos0 .. q_pos0 + n_q - 1 must lie inside the cache (q_pos0 %d, n_q %d, n_kv %d)",
+          d->q_pos0, d->n_q, d->n_kv);
+  REQUIRE((int64_t)d->batch * d->n_q <= (1ll << 30), DSA_ERR_UNSUPPORTED, "batch * n_q too large");
+  REQUIRE(k_new && k_idx && k_scale, DSA_ERR_INVALID_ARG, "null key pointer");
+  REQUIRE(k_dtype == 0 || k_dtype == 1, DSA_ERR_INVALID_ARG, "k_dtype must be 0 (f32) or 1 (bf16), got %d", k_dtype);
+  REQUIRE(d->idx_dim >= 4 && d->idx_dim <= 16384 && d->idx_dim % 4 == 0, DSA_ERR_UNSUPPORTED,
+          "idx_dim must be a multiple of 4 in [4, 16384] (got %d)", d->idx_dim);
+  REQUIRE(aligned(k_new, k_dtype == 0 ? 16 : 8) && aligned(k_idx, 4) && aligned(k_scale, 4), DSA_ERR_INVALID_ARG,
+          "misaligned key pointer");
+  REQUIRE((kv_new == nullptr) == (kv == nullptr), DSA_ERR_INVALID_ARG, "kv_new and kv must both be given or both NULL");
+  if (kv) {
+    REQUIRE(d->dim_qk >= 8 && d->dim_qk % 8 == 0, DSA_ERR_UNSUPPORTED, "dim_qk must be a multiple of 8 (got %d)",
+            d->dim_qk);
+    REQUIRE(aligned(kv_new, 16) && aligned(kv, 16), DSA_ERR_INVALID_ARG, "kv_new and kv must be 16-byte aligned");
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  const int64_t n = (int64_t)d->batch * d->n_q;
+  int st = hip_status(dsa::launch_quantize(k_new, k_dtype, n, d->idx_dim, d->n_q, d->n_kv, d->q_pos0, k_idx, k_scale, s),
+                      "cache append (keys)");
+  if (st != DSA_OK || !kv) return st;
+  return hip_status(dsa::launch_copy_rows(kv_new, kv, n, d->dim_qk, d->n_q, d->n_kv, d->q_pos0, s),
+                    "cache append (latents)");
 }
 
 }  // extern "C"

@@ -56,4 +56,13 @@ hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st);
 bool attn_dims_supported(int H, int Dk, int Dv);
 int topk_max_kv();
 
+// Per-token E4M3 quantisation of n_tokens rows of len values (dtype 0 f32,
+// 1 bf16); token tok goes to output row (tok / group) * out_stride + out_off
+// + tok % group of codes/scales.
+hipError_t launch_quantize(const void* x, int dtype, int64_t n_tokens, int32_t len, int32_t group,
+                           int64_t out_stride, int64_t out_off, uint8_t* codes, float* scales, hipStream_t st);
+// Copy of n_rows bf16 rows of row_len (a multiple of 8) with the same row mapping.
+hipError_t launch_copy_rows(const uint16_t* src, uint16_t* dst, int64_t n_rows, int32_t row_len, int32_t group,
+                            int64_t out_stride, int64_t out_off, hipStream_t st);
+
 }  // namespace dsa

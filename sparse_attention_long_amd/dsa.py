@@ -19,7 +19,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 # Every symbol include/dsa.h declares.
 EXPORTS = (
     "dsa_indexer_scores", "dsa_topk", "dsa_attn_workspace_size", "dsa_sparse_mla_attn",
-    "dsa_forward_workspace_size", "dsa_forward", "dsa_status_string", "dsa_last_error", "dsa_version",
+    "dsa_forward_workspace_size", "dsa_forward", "dsa_quantize_e4m3", "dsa_cache_append", "dsa_status_string",
+    "dsa_last_error", "dsa_version",
 )
 
 
@@ -60,10 +61,13 @@ def lib():
         L.dsa_forward_workspace_size.argtypes = [D]
         L.dsa_forward_workspace_size.restype = ctypes.c_size_t
         L.dsa_forward.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dsa_quantize_e4m3.argtypes = [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
+        L.dsa_cache_append.argtypes = [D, _P, ctypes.c_int, _P, _P, _P, _P, _P]
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.restype = ctypes.c_char_p
-        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_version"):
+        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_quantize_e4m3",
+                  "dsa_cache_append", "dsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -122,3 +126,25 @@ def dsa_forward(dims: Dims, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_sca
     _check(lib().dsa_forward(ctypes.byref(dims), _ptr(q_idx), _ptr(q_scale), _ptr(w_idx), _ptr(k_idx),
                              _ptr(k_scale), _ptr(q), _ptr(kv), float(sm_scale), _ptr(out), _ptr(lse),
                              _ptr(idx_out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def _dtype_code(x, dtype):
+    if dtype is not None:
+        return int(dtype)
+    name = str(getattr(x, "dtype", ""))
+    if "float32" in name:
+        return 0
+    if "bfloat16" in name or "int16" in name:
+        return 1
+    raise ValueError("pass dtype=0 (f32) or dtype=1 (bf16) for raw pointers")
+
+
+def dsa_quantize_e4m3(x, n_tokens: int, token_len: int, codes, scales, dtype=None, stream=None):
+    """x: f32 or bf16 (bits in an int16 / bfloat16 tensor); codes uint8; scales f32."""
+    _check(lib().dsa_quantize_e4m3(_ptr(x), _dtype_code(x, dtype), int(n_tokens), int(token_len), _ptr(codes),
+                                   _ptr(scales), _stream(stream)))
+
+
+def dsa_cache_append(dims: Dims, k_new, k_idx, k_scale, kv_new=None, kv=None, k_dtype=None, stream=None):
+    _check(lib().dsa_cache_append(ctypes.byref(dims), _ptr(k_new), _dtype_code(k_new, k_dtype), _ptr(kv_new),
+                                  _ptr(k_idx), _ptr(k_scale), _ptr(kv), _stream(stream)))

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert dsa.dsa_version() == 100
+    assert dsa.dsa_version() == 101
     L = dsa.lib()
     assert L.dsa_status_string(0) == b"ok"
     assert L.dsa_status_string(3) == b"workspace too small"
@@ -102,3 +102,27 @@ def test_forward_workspace_plan():
         dsa.dsa_forward(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE, ws=FAKE, ws_bytes=ws - 1, stream=0)
     assert e.value.status == dsa.dsa.ERR_WORKSPACE
     assert dsa.dsa_forward_workspace_size(_dims(heads=7, dim_qk=100)) == 0   # unsupported dims
+
+
+def test_quantize_validation():
+    for args, status in (((FAKE, 2, 4, 128), dsa.dsa.ERR_INVALID_ARG),      # bad dtype
+                         ((FAKE, 0, 4, 130), dsa.dsa.ERR_UNSUPPORTED),      # length not a multiple of 4
+                         ((FAKE, 0, 4, 20000), dsa.dsa.ERR_UNSUPPORTED),    # too long
+                         ((FAKE + 8, 0, 4, 128), dsa.dsa.ERR_INVALID_ARG),  # f32 input not 16-byte aligned
+                         ((0, 0, 4, 128), dsa.dsa.ERR_INVALID_ARG)):        # null
+        x, dt, n, L = args
+        with pytest.raises(dsa.DSAError) as e:
+            dsa.dsa.dsa_quantize_e4m3(x, n, L, FAKE, FAKE, dtype=dt, stream=0)
+        assert e.value.status == status
+
+
+def test_cache_append_validation():
+    with pytest.raises(dsa.DSAError) as e:   # new positions past the cache
+        dsa.dsa.dsa_cache_append(_dims(n_q=2, n_kv=8, q_pos0=7), FAKE, FAKE, FAKE, k_dtype=0, stream=0)
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+    with pytest.raises(dsa.DSAError) as e:   # latent source without a latent cache
+        dsa.dsa.dsa_cache_append(_dims(n_q=1, n_kv=8, q_pos0=7), FAKE, FAKE, FAKE, kv_new=FAKE, k_dtype=0, stream=0)
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa.dsa_cache_append(_dims(n_q=1, n_kv=8, q_pos0=7, idx_dim=6), FAKE, FAKE, FAKE, k_dtype=1, stream=0)
+    assert e.value.status == dsa.dsa.ERR_UNSUPPORTED

@@ -269,3 +269,64 @@ def test_cost_figures_of_the_pages():
     assert 128 * (576 + 512) == 139264
     assert round(139264 / 8192) == 17
     assert abs(2048 / 131072 - 0.016) < 0.0005
+
+
+# ------------------------------------------------------------------ FP8 quantisation
+def test_quantize_matches_torch_float8_and_the_input_generator():
+    # The per-token quantiser against two independent implementations of the
+    # same definition: torch's float8_e4m3fn conversion (round to nearest
+    # even; every quotient here is at most 448 * (1 + 2^-23)) applied to the
+    # scaled values, and the input generator's own encoder.
+    from synth import gen
+    rs = np.random.RandomState(11)
+    x = (rs.randn(300, 128) * np.exp(rs.randn(300, 1) * 6)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :] = -0.0
+    x[2, 5] = -3e-7
+    codes, scales = O.quantize_e4m3_tokens(x)
+    assert scales[0] == 1.0 and np.all(codes[0] == 0) and np.all(codes[1] == 0x80)
+    y = (x / scales[:, None]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    c2, s2 = gen.quantize_tokens_e4m3(x)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+
+
+def test_quantize_ties_saturation_and_exact_values():
+    # amax = 448 gives scale 1, so the codes are those of x itself.
+    vals = O.E4M3_VALUES[:0x7F]
+    mids = (vals[:-1] + vals[1:]) / 2                       # exact midpoints
+    row = np.concatenate([[448.0], vals, mids, [-1.0625]]).astype(np.float32)
+    pad = (-len(row)) % 4
+    row = np.concatenate([row, np.zeros(pad, np.float32)])
+    codes, scales = O.quantize_e4m3_tokens(row[None, :])
+    assert scales[0] == 1.0
+    c = codes[0]
+    n = len(vals)
+    assert np.array_equal(c[1:1 + n], np.arange(n, dtype=np.uint8))           # representable: exact
+    tie = c[1 + n:1 + n + len(mids)]
+    assert np.all(tie % 2 == 0) and np.all((tie == np.arange(len(mids))) | (tie == np.arange(1, len(mids) + 1)))
+    assert c[1 + n + len(mids)] == (0x80 | 0x38)             # -1.0625 -> -1.0 (even mantissa)
+    # A token whose amax / (amax / 448) rounds above 448 saturates to 0x7E.
+    rs = np.random.RandomState(13)
+    for _ in range(10000):
+        amax = np.float32(rs.uniform(1, 100))
+        sc = np.float32(amax / np.float32(448.0))
+        if np.float32(amax / sc) > np.float32(448.0):
+            break
+    else:
+        raise AssertionError("no rounding-up quotient found")
+    codes, _ = O.quantize_e4m3_tokens(np.array([[amax, 0, 0, 0]], np.float32))
+    assert codes[0, 0] == 0x7E
+
+
+def test_quantize_round_trip_error_bound():
+    # |decode(code) * scale - x| <= half a unit in the last place of the
+    # E4M3 grid at |x / scale| (2^-10 * scale in the subnormal range).
+    rs = np.random.RandomState(12)
+    x = (rs.standard_cauchy((100, 64))).astype(np.float32)
+    codes, scales = O.quantize_e4m3_tokens(x)
+    back = O.e4m3_decode(codes) * scales[:, None].astype(np.float64)
+    a = np.abs(x.astype(np.float64) / scales[:, None])
+    ulp = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(back - x) <= 0.5 * ulp * scales[:, None] * (1 + 1e-6) + 1e-30)
