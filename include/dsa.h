@@ -111,6 +111,10 @@ int dsa_topk(const dsa_dims* dims, const float* scores, int64_t ld, int32_t* idx
  *   ws   workspace of at least dsa_attn_workspace_size(dims) bytes (may be
  *        NULL when that size is 0).
  * QK^T and PV run on bf16 MFMA with fp32 accumulation; softmax is fp32.
+ * One sequence's latent cache must be below 4 GiB (n_kv * Dk * 2 bytes <
+ * 2^32, i.e. n_kv < 3,728,270 at Dk = 576): rows are addressed by 32-bit
+ * offsets from the sequence's base.  Larger caches return
+ * DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_attn_workspace_size(const dsa_dims* dims);
 int dsa_sparse_mla_attn(const dsa_dims* dims, const uint16_t* q, const uint16_t* kv, const int32_t* idx,

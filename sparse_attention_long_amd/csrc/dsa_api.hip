@@ -61,6 +61,9 @@ int check_attn_dims(const dsa_dims* d) {
           "attention dims (heads %d, dim_qk %d, dim_v %d) not built; supported: dim_qk 576 / dim_v 512 "
           "with heads <= 128, dim_qk 80 / dim_v 64 with heads <= 32",
           d->heads, d->dim_qk, d->dim_v);
+  // The row gathers address a sequence's latent cache with 32-bit byte offsets.
+  REQUIRE((uint64_t)d->n_kv * (uint64_t)d->dim_qk * 2u < (1ull << 32), DSA_ERR_UNSUPPORTED,
+          "one sequence's latent cache (n_kv %d x dim_qk %d bf16) must be below 4 GiB", d->n_kv, d->dim_qk);
   return DSA_OK;
 }
 

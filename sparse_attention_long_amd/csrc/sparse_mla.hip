@@ -9,7 +9,8 @@
 //
 // Work shape (gfx950): one workgroup per (query row, split of the selected
 // slots); wave w owns heads [32w, 32w+32).  Rows are gathered 32 at a time
-// into a double-buffered LDS tile.  Per chunk and wave:
+// into a three-deep ring of LDS tiles by global_load_lds DMA, two chunks
+// ahead.  Per chunk and wave:
 //   S^T[32 rows x 32 heads] = C[32 x Dk] . Q^T[Dk x 32]   (v_mfma_f32_32x32x16_bf16,
 //        A = C from LDS, B = the wave's Q^T kept in registers for the whole row)
 //   online softmax per head (lane-local: the S^T layout puts one head per lane)
@@ -24,6 +25,13 @@
 // (log2 units) is the row recomputed once with the true maximum as the
 // reference.  No O rescale is ever needed, which keeps the 32x512 fp32
 // accumulator of each wave in the AGPR file without spills.
+//
+// A wave runs one chunk's phases back to back (gather issue, QK, softmax,
+// PV), so the non-MFMA phases are kept short: the S^T chain accumulates in
+// VGPRs (next to the softmax that reads it, not in the AGPR file next to
+// O^T), the softmax folds scale and reference into one fma per logit and
+// masks only a row's last chunk, and a row copy costs one lane read and one
+// VALU op (scalar sequence base + 32-bit offset).
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -80,21 +88,19 @@ __device__ __forceinline__ int piece_pos(int r, int p) {
 }
 
 // Gather one chunk's rows into a tile with global_load_lds_dwordx4 (issued
-// from inline asm, see dma_x4): each wave instruction fills 64 consecutive
-// 16-byte LDS pieces, lane l filling piece base + l from the global row
-// piece that belongs there.  Instruction j goes to wave j % NW, so every
-// wave issues kDma / NW instructions; issue(jj) sends this wave's jj-th.  An
-// invalid row index reads row 0 (finite data, masked out of the softmax).
-// Set-up computes the chunk's row addresses once (one 64-bit product per
-// lane); each row copy then needs two lane reads into SGPRs, one offset
-// VGPR and the M0 set-up.
+// from inline asm, see dma_x4), for the shapes whose rows are not one wave
+// instruction long: each wave instruction fills 64 consecutive 16-byte LDS
+// pieces, lane l filling piece base + l from the global row piece that
+// belongs there, with a 64-bit address per lane.  Instruction j goes to wave
+// j % NW, so every wave issues kDma / NW instructions.  An invalid row index
+// reads row 0 (finite data, masked out of the softmax).
 template <int DK, int DV, int NW>
 struct ChunkGather {
   using C = Cfg<DK, DV, NW>;
+  static_assert(!C::kRowDma, "row-sized shapes use RowGather");
   uint16_t* tile;
   const uint16_t* kvb;
   int row_of_lane;    // lane j < 32 holds the chunk's j-th row index (or < 0)
-  uint32_t addr_lo, addr_hi;   // lane j < 32: byte address of that row
   int wave;
 
   __device__ __forceinline__ void init(uint16_t* t, const uint16_t* kv, int rol) {
@@ -102,23 +108,11 @@ struct ChunkGather {
     kvb = kv;
     row_of_lane = max(rol, 0);
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t ad = (uint64_t)(uintptr_t)(kvb + (int64_t)row_of_lane * DK);
-    addr_lo = (uint32_t)ad;
-    addr_hi = (uint32_t)(ad >> 32);
   }
   __device__ __forceinline__ void issue(int jj) const {
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));   // keep the cheap per-lane offsets here, do not hoist them
+    const int lane = threadIdx.x & 63;
     const int j = jj * NW + wave;   // wave-uniform instruction index
-    // Whether instruction jj of every wave lies in part A or part B is known
-    // at compile time for the shapes built here (no wave straddles).
-    const bool in_a = (jj + 1) * NW <= C::kDmaA ? true : (jj * NW >= C::kDmaA ? false : j < C::kDmaA);
-    if (C::kRowDma && in_a) {
-      // one row per instruction: scalar row base + per-lane swizzled piece
-      const uint64_t rowp = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, j) << 32) |
-                            (uint32_t)__builtin_amdgcn_readlane((int)addr_lo, j);
-      dma_x4_s(16u * (uint32_t)(lane ^ swz_a(j)), (const void*)(uintptr_t)rowp, lds_addr(tile + j * C::kRA * 8));
-    } else if (in_a) {
+    if (j < C::kDmaA) {
       const int q = j * kWave + lane;             // piece of the contiguous part A
       const int r = q / C::kPA, pp = q % C::kPA;
       const int s = __shfl(row_of_lane, r, kWave);
@@ -134,6 +128,44 @@ struct ChunkGather {
   __device__ __forceinline__ void issue_all() const {
 #pragma unroll
     for (int jj = 0; jj < C::kDma / NW; ++jj) issue(jj);
+  }
+};
+
+// Gather for the shapes whose part-A rows are exactly one wave instruction
+// (Dv = 512) with 4 waves: every copy takes the sequence's cache base as its
+// scalar address and a 32-bit per-lane byte offset (a sequence's latent cache
+// is below 4 GiB), so a row copy costs one lane read and one VALU op.  Wave w
+// copies rows j = 4*jj + w (jj < 8) of part A, whose piece swizzle is jj % 4,
+// and the part-B block of rows 8w .. 8w+7.
+template <int DK, int DV, int NW>
+struct RowGather {
+  using C = Cfg<DK, DV, NW>;
+  static_assert(C::kRowDma && NW == 4 && C::kDmaA == kChunk && C::kDmaB == NW, "row gather shape");
+  uint32_t off_a;   // lane j < 32: byte offset of chunk row j
+  uint32_t off_b;   // byte offset of this lane's part-B piece
+  uint32_t lane16;  // 16 * lane
+
+  // Chunk row whose index lane `lane` must supply for part B.
+  __device__ __forceinline__ static int row_b(int wave, int lane) { return (wave * kWave + lane) / C::kPB; }
+
+  __device__ __forceinline__ void init(int ra, int rb, int wave) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));   // keep the per-lane terms here, do not hoist them
+    lane16 = 16u * (uint32_t)lane;
+    off_a = (uint32_t)max(ra, 0) * (uint32_t)(DK * 2);
+    const int q = wave * kWave + lane;
+    const int r = q / C::kPB, pp = q % C::kPB;
+    off_b = (uint32_t)max(rb, 0) * (uint32_t)(DK * 2) + 16u * (uint32_t)(C::kPA + (pp ^ (r & (C::kPB - 1))));
+  }
+  __device__ __forceinline__ void issue_all(uint16_t* tile, const uint16_t* kvb, int wave) const {
+    const uint32_t t0 = lds_addr(tile);
+#pragma unroll
+    for (int jj = 0; jj < C::kDmaA / NW; ++jj) {
+      const int j = jj * NW + wave;
+      const uint32_t so = (uint32_t)__builtin_amdgcn_readlane((int)off_a, j);
+      dma_x4_s((lane16 ^ (16u * (uint32_t)(jj & 3))) + so, kvb, t0 + (uint32_t)j * (C::kRA * 16));
+    }
+    dma_x4_s(off_b, kvb, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
   }
 };
 
@@ -168,7 +200,12 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid,
     if (2 * ks < C::kPA) return *(const v8bf*)((ks & 1 ? a_odd : a_even) + 32 * (ks >> 1));
     return *(const v8bf*)(tb + piece_pos<DK, DV, NW>(col, 2 * ks + half));
   };
-  v16f st = {};
+  // The S^T chain is written as inline asm so that its accumulator is a
+  // VGPR tuple (the compiler would put it in AGPRs, next to O^T, and move an
+  // O^T tile out and back every chunk).  The compiler does not see these as
+  // MFMAs, so the wait states before the first VALU read of the result are
+  // explicit (32x32 XDL result -> VALU read: 18 on gfx950; 21 given).
+  v16f st;
   v8bf abuf[kLookA];
 #pragma unroll
   for (int j = 0; j < kLookA; ++j) abuf[j] = load_a(j);
@@ -176,27 +213,37 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid,
   for (int ks = 0; ks < C::kKS; ++ks) {
     const v8bf cur = abuf[ks % kLookA];
     if (ks + kLookA < C::kKS) abuf[ks % kLookA] = load_a(ks + kLookA);
-    st = mfma_bf16_32x32x16(cur, qb[ks], st);
+    if (ks == 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(cur), "v"(qb[ks]));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(st) : "v"(cur), "v"(qb[ks]));
   }
-  // ---- mask, scale, chunk max
-  const uint32_t vh = valid >> (4 * half);
-  const bool all_valid = valid == 0xFFFFFFFFu;
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(st));
+  // ---- mask (only a row's last chunk can hold padding), chunk max
   float z[16];
-  float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 8 * (j >> 2) + (j & 3);       // row minus 4*half
-    z[j] = (all_valid || ((vh >> r) & 1u)) ? st[j] * zscale : -INFINITY;
-    mx = fmaxf(mx, z[j]);
+  for (int j = 0; j < 16; ++j) z[j] = st[j];
+  if (valid != 0xFFFFFFFFu) {   // wave-uniform
+    const uint32_t vh = valid >> (4 * half);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + (j & 3);       // row minus 4*half
+      if (!((vh >> r) & 1u)) z[j] = -INFINITY;
+    }
   }
-  mx = max_halves(mx);
+  float mx = z[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, z[j]);
+  // zscale > 0, so the scaled maximum is the scaled raw maximum
+  mx = max_halves(mx) * zscale;
   if (rs.m_ref == -INFINITY) rs.m_ref = mx;
   rs.m_seen = fmaxf(rs.m_seen, mx);
   // ---- probabilities, packed as the P^T operand (K order = S^T row order)
+  const float nref = -rs.m_ref;
   v8bf pb[2];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float pj = __builtin_amdgcn_exp2f(z[j] - rs.m_ref);
+    const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(z[j], zscale, nref));
     rs.l_sum += pj;
     pb[j >> 3][j & 7] = (__bf16)pj;
   }
@@ -298,20 +345,37 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   // has passed the barrier of chunk c (so nobody still reads chunk c-1's
   // tile); before that barrier each wave waits until its own part of chunk c
   // has landed while chunk c+1's DMA stays in flight.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto gather = [&](int c, uint16_t* fill, int ra, int rb) {
+    if constexpr (C::kRowDma) {
+      RowGather<DK, DV, NW> g;
+      g.init(ra, rb, wv);
+      g.issue_all(fill, kvb, wv);
+    } else {
+      ChunkGather<DK, DV, NW> g;
+      g.init(fill, kvb, ra);
+      g.issue_all();
+    }
+  };
+  auto rb_of = [&](int c) {
+    if constexpr (C::kRowDma) return sidx[c * kChunk + RowGather<DK, DV, NW>::row_b(wv, lane)];
+    else return 0;
+  };
   auto step = [&](int c, const uint16_t* cur, uint16_t* fill) {
+    // The slot indices are read before the barrier (they do not change after
+    // the prologue), so their LDS latency overlaps the wait.
+    const int cn = min(c + 2, nchunks - 1);
+    const int rv = sidx[c * kChunk + (lane & 31)];
+    const int ra = sidx[cn * kChunk + (lane & 31)];
+    const int rb = rb_of(cn);
     // Each wave waits until its own copies of chunk c landed (chunk c+1's
     // stay in flight); the barrier then publishes the tile.  A compiler-level
     // memory barrier keeps LDS accesses on their side of it; the tile
     // refilled next was last read (and consumed) in chunk c-1.
     if (c + 1 < nchunks) wait_vm<ndma>(); else wait_vm<0>();
     asm volatile("s_barrier" ::: "memory");
-    if (c + 2 < nchunks) {
-      ChunkGather<DK, DV, NW> g;
-      g.init(fill, kvb, sidx[(c + 2) * kChunk + (lane & 31)]);
-      g.issue_all();
-    }
-    const uint32_t valid =
-        (uint32_t)__builtin_amdgcn_ballot_w64(lane < kChunk && sidx[c * kChunk + (lane & 31)] >= 0);
+    if (c + 2 < nchunks) gather(c + 2, fill, ra, rb);
+    const uint32_t valid = (uint32_t)__builtin_amdgcn_ballot_w64(lane < kChunk && rv >= 0);
     if (valid != 0u) attend_chunk<DK, DV, NW>(cur, valid, qb, zscale, rs);
   };
 
@@ -319,11 +383,8 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < C::kNT; ++t) rs.o[t] = (v16f){};
     rs.l_sum = 0.f;
-    {
-      ChunkGather<DK, DV, NW> g;
-      if (nchunks > 0) { g.init(tile0, kvb, sidx[lane & 31]); g.issue_all(); }
-      if (nchunks > 1) { g.init(tile1, kvb, sidx[kChunk + (lane & 31)]); g.issue_all(); }
-    }
+    if (nchunks > 0) gather(0, tile0, sidx[lane & 31], rb_of(0));
+    if (nchunks > 1) gather(1, tile1, sidx[kChunk + (lane & 31)], rb_of(1));
     for (int c = 0; c < nchunks; c += 3) {
       step(c, tile0, tile2);
       if (c + 1 >= nchunks) break;

@@ -91,6 +91,14 @@ def test_attention_validation_and_workspace():
     assert e.value.status == dsa.dsa.ERR_WORKSPACE
     # many rows: no split, no workspace
     assert dsa.dsa_attn_workspace_size(_dims(n_q=4096, n_kv=4096, topk=2048)) == 0
+    # one sequence's latent cache must stay below 4 GiB (32-bit row offsets)
+    limit = (1 << 32) // (576 * 2)                       # 3,728,270 rows of 1152 B
+    assert dsa.dsa_attn_workspace_size(_dims(n_q=1, n_kv=limit, q_pos0=limit - 1, topk=2048)) > 0
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa_sparse_mla_attn(_dims(n_q=1, n_kv=limit + 1, q_pos0=limit, topk=2048), FAKE, FAKE, FAKE, 0.1, FAKE,
+                                ws=FAKE, ws_bytes=1 << 30, stream=0)
+    assert e.value.status == dsa.dsa.ERR_UNSUPPORTED and "4 GiB" in str(e.value)
+    assert dsa.dsa_attn_workspace_size(_dims(n_q=1, n_kv=limit + 1, q_pos0=limit, topk=2048)) == 0
 
 
 def test_forward_workspace_plan():
