@@ -172,6 +172,77 @@ int dsa_quantize_e4m3(const void* x, int x_dtype, int64_t n_tokens, int32_t toke
 int dsa_cache_append(const dsa_dims* dims, const void* k_new, int k_dtype, const uint16_t* kv_new,
                      uint8_t* k_idx, float* k_scale, uint16_t* kv, void* stream);
 
+/*
+ * Paged, variable-length caches (the analysis page, Sec. 5.1: the sequences
+ * of one batch have their own context lengths, which limit each row to
+ * min(k, t) candidates, and a row's selected entries are gathered from cache
+ * pages, few and contiguous or many and scattered).
+ *
+ * Pools of num_pages pages of page_size tokens replace the [B, n_kv, ...]
+ * caches:
+ *   k_idx   [num_pages * page_size, d_I]  e4m3
+ *   k_scale [num_pages * page_size]       f32
+ *   kv      [num_pages * page_size, Dk]   bf16
+ * Token s of sequence b is pool row
+ *   page_table[b * max_pages + s / page_size] * page_size + s % page_size.
+ * With page_table NULL the caches keep the dense [B, n_kv, ...] layout of the
+ * calls above and only the lengths vary.
+ *
+ * Sequence b holds seq_lens[b] tokens; its n_q query rows are its last n_q
+ * tokens, row i at position seq_lens[b] - n_q + i (a decode step: n_q = 1,
+ * p = seq_lens[b] - 1, the new token sees itself), so row i has
+ * seq_lens[b] - n_q + i + 1 candidates.  dims->n_kv bounds the lengths (and
+ * is the scores row length); dims->q_pos0 is not used.  Query-side tensors
+ * (q_idx, q_scale, w_idx, q, out, lse, scores, idx) keep their [B, n_q, ...]
+ * layouts, and idx holds token indices s, not pool rows.
+ *
+ * seq_lens and page_table are device arrays whose values the host does not
+ * read: a length outside [n_q, n_kv] is clamped into it and a page entry
+ * outside [0, num_pages) is clamped into it (the results are then wrong, but
+ * no access leaves the buffers).  Workspace sizes are those of the dense
+ * calls (dsa_attn_workspace_size, dsa_forward_workspace_size).
+ */
+typedef struct {
+  const int32_t* seq_lens;    /* device [B], required                                 */
+  const int32_t* page_table;  /* device [B, max_pages], or NULL for dense caches      */
+  int32_t page_size;          /* tokens per page, a positive multiple of 64            */
+  int32_t max_pages;          /* row stride of page_table; max_pages * page_size >= n_kv */
+  int32_t num_pages;          /* pages per pool; num_pages * page_size < 2^31          */
+} dsa_paged_kv;
+
+/* dsa_indexer_scores over a paged / variable-length key cache.  Row i of
+ * sequence b is written for s < seq_lens[b] - n_q + i + 1. */
+int dsa_indexer_scores_paged(const dsa_dims* dims, const dsa_paged_kv* layout, const uint8_t* q_idx,
+                             const float* q_scale, const uint16_t* w_idx, const uint8_t* k_idx,
+                             const float* k_scale, float* scores, int64_t ld, void* stream);
+/* dsa_topk with per-sequence lengths (only layout->seq_lens is used). */
+int dsa_topk_paged(const dsa_dims* dims, const dsa_paged_kv* layout, const float* scores, int64_t ld,
+                   int32_t* idx, void* stream);
+/* dsa_sparse_mla_attn over a paged / variable-length latent cache; entries
+ * of idx outside [0, seq_lens[b]) are skipped.  A pool may exceed 4 GiB. */
+int dsa_sparse_mla_attn_paged(const dsa_dims* dims, const dsa_paged_kv* layout, const uint16_t* q,
+                              const uint16_t* kv, const int32_t* idx, float sm_scale, uint16_t* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream);
+/* dsa_forward over paged / variable-length caches: equal, bit for bit, to
+ * the three paged calls one after the other. */
+int dsa_forward_paged(const dsa_dims* dims, const dsa_paged_kv* layout, const uint8_t* q_idx,
+                      const float* q_scale, const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale,
+                      const uint16_t* q, const uint16_t* kv, float sm_scale, uint16_t* out, float* lse,
+                      int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Locality counters of the selections (Sec. 5.1 of the analysis page: the
+ * distinct pages, the contiguous runs and the hits per page of each row).
+ * For every row of idx [B, n_q, topk] (ascending token indices as dsa_topk
+ * writes them; entries < 0 skipped):
+ *   stats[b, i, 0] = number of distinct pages s / page_size
+ *   stats[b, i, 1] = number of maximal runs of consecutive indices
+ *   stats[b, i, 2] = largest number of selected tokens on one page
+ * stats is [B, n_q, 3] int32; an empty row gives 0 0 0.  Uses batch, n_q and
+ * topk of dims; page_size >= 1.
+ */
+int dsa_gather_stats(const dsa_dims* dims, int32_t page_size, const int32_t* idx, int32_t* stats, void* stream);
+
 /* Status text, thread-local last error message, ABI version (major*100+minor). */
 const char* dsa_status_string(int status);
 const char* dsa_last_error(void);

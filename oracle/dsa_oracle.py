@@ -212,3 +212,38 @@ def dsa_row(q_idx_t, w_t, k_idx, q_t, kv, p: int, k: int, sm_scale: float, dim_v
     sel = topk_row(sc, k)
     o, lse = sparse_mla_row(q_t, kv, sel, sm_scale, dim_v)
     return sc, sel, o, lse
+
+
+# ----------------------------------------------------------------- paged / variable-length caches
+# The analysis page, Sec. 5.1: rows of one batch have their own context length
+# (per-sequence lengths limit each row to min(k, t) candidates), the selected
+# entries of a row may sit in a few contiguous cache pages or be spread over
+# many, and a profiler should count the distinct pages, the contiguous runs
+# and the hits per page of a row's selection.
+def paged_gather(pool, page_row, page_size: int, n: int) -> np.ndarray:
+    """The first n logical tokens of one sequence from a page pool (axis 0 =
+    physical token slot): logical token s lives in slot
+    page_row[s // page_size] * page_size + s % page_size."""
+    s = np.arange(n)
+    slots = np.asarray(page_row, dtype=np.int64)[s // page_size] * page_size + s % page_size
+    return np.asarray(pool)[slots]
+
+
+def varlen_positions(seq_len: int, n_q: int) -> list:
+    """Absolute positions of the n_q query rows of a sequence with seq_len
+    cached tokens: its last n_q tokens (decode: n_q = 1, p = seq_len - 1)."""
+    return [seq_len - n_q + i for i in range(n_q)]
+
+
+def gather_stats(sel, page_size: int):
+    """Locality of one row's selection (padding < 0 skipped): the number of
+    distinct cache pages it touches, the number of maximal runs of
+    consecutive token indices, and the largest number of selected tokens on
+    one page.  An empty selection gives (0, 0, 0)."""
+    s = np.asarray(sel, dtype=np.int64)
+    s = np.sort(s[s >= 0])
+    if s.size == 0:
+        return 0, 0, 0
+    pages, hits = np.unique(s // page_size, return_counts=True)
+    runs = 1 + int(np.count_nonzero(np.diff(s) != 1))
+    return int(pages.size), runs, int(hits.max())

@@ -61,10 +61,48 @@ int check_attn_dims(const dsa_dims* d) {
           "attention dims (heads %d, dim_qk %d, dim_v %d) not built; supported: dim_qk 576 / dim_v 512 "
           "with heads <= 128, dim_qk 80 / dim_v 64 with heads <= 32",
           d->heads, d->dim_qk, d->dim_v);
-  // The row gathers address a sequence's latent cache with 32-bit byte offsets.
+  return DSA_OK;
+}
+
+// Dense caches: the row gathers address a sequence's latent cache with
+// 32-bit byte offsets (page pools use 64-bit row addresses).
+int check_dense_kv_size(const dsa_dims* d) {
   REQUIRE((uint64_t)d->n_kv * (uint64_t)d->dim_qk * 2u < (1ull << 32), DSA_ERR_UNSUPPORTED,
           "one sequence's latent cache (n_kv %d x dim_qk %d bf16) must be below 4 GiB", d->n_kv, d->dim_qk);
   return DSA_OK;
+}
+
+// Paged / variable-length layout: host checks of the descriptor (the device
+// arrays themselves are clamped by the kernels).  Fills `pk`.
+int check_paged(const dsa_dims* d, const dsa_paged_kv* p, dsa::PagedKV* pk) {
+  REQUIRE(p != nullptr, DSA_ERR_INVALID_ARG, "paged layout is NULL");
+  REQUIRE(p->seq_lens != nullptr && aligned(p->seq_lens, 4), DSA_ERR_INVALID_ARG,
+          "seq_lens must be a non-null, 4-byte aligned device pointer");
+  *pk = dsa::PagedKV{};
+  pk->seq_lens = p->seq_lens;
+  pk->n_q_total = d->n_q;
+  if (p->page_table) {
+    REQUIRE(aligned(p->page_table, 4), DSA_ERR_INVALID_ARG, "page_table must be 4-byte aligned");
+    REQUIRE(p->page_size >= 64 && p->page_size % 64 == 0, DSA_ERR_UNSUPPORTED,
+            "page_size must be a positive multiple of 64 (got %d)", p->page_size);
+    REQUIRE((int64_t)p->max_pages * p->page_size >= d->n_kv, DSA_ERR_INVALID_ARG,
+            "max_pages (%d) x page_size (%d) must cover n_kv (%d)", p->max_pages, p->page_size, d->n_kv);
+    REQUIRE(p->num_pages >= 1 && (int64_t)p->num_pages * p->page_size < (1ll << 31), DSA_ERR_UNSUPPORTED,
+            "num_pages (%d) x page_size (%d) must be in [1, 2^31)", p->num_pages, p->page_size);
+    pk->page_table = p->page_table;
+    pk->page_size = p->page_size;
+    pk->max_pages = p->max_pages;
+    pk->num_pages = p->num_pages;
+  }
+  return DSA_OK;
+}
+
+// dims for the paged calls: positions come from seq_lens, so q_pos0 plays no
+// part (set to 0 for the common checks).
+dsa_dims paged_dims(const dsa_dims* d) {
+  dsa_dims dd = *d;
+  dd.q_pos0 = 0;
+  return dd;
 }
 
 // Split of the selected slots across workgroups for attention: enough
@@ -118,8 +156,9 @@ int hip_status(hipError_t e, const char* what) {
 
 dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w,
                               const uint8_t* k_idx, const float* k_scale, float* scores, int64_t ld,
-                              int64_t i0, int rows, int64_t sc_rows_b) {
-  dsa::IndexerArgs a;
+                              int64_t i0, int rows, int64_t sc_rows_b, const dsa::PagedKV& pk) {
+  dsa::IndexerArgs a{};
+  a.pk = pk;
   a.q_idx = q_idx + i0 * d->idx_heads * d->idx_dim;
   a.q_scale = q_scale + i0;
   a.w = w + i0 * d->idx_heads;
@@ -131,7 +170,7 @@ dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const flo
   a.sc_rows_b = sc_rows_b;
   a.B = d->batch;
   a.rows = rows;
-  a.pos0 = d->q_pos0 + (int)i0;
+  a.pos0 = (pk.seq_lens ? 0 : d->q_pos0) + (int)i0;
   a.S = d->n_kv;
   a.HI = d->idx_heads;
   a.dI = d->idx_dim;
@@ -142,7 +181,7 @@ dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const flo
 
 extern "C" {
 
-int dsa_version(void) { return 101; }
+int dsa_version(void) { return 102; }
 
 const char* dsa_status_string(int status) {
   switch (status) {
@@ -157,8 +196,13 @@ const char* dsa_status_string(int status) {
 
 const char* dsa_last_error(void) { return g_last_error; }
 
-int dsa_indexer_scores(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
-                       const uint8_t* k_idx, const float* k_scale, float* scores, int64_t ld, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int indexer_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx, const float* q_scale,
+                 const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale, float* scores, int64_t ld,
+                 void* stream) {
   int st;
   if ((st = check_common(d)) != DSA_OK) return st;
   if ((st = check_indexer_dims(d)) != DSA_OK) return st;
@@ -168,12 +212,13 @@ int dsa_indexer_scores(const dsa_dims* d, const uint8_t* q_idx, const float* q_s
           DSA_ERR_INVALID_ARG, "misaligned scale/score/weight pointer");
   REQUIRE(ld >= d->n_kv, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= n_kv (%d)", (long long)ld, d->n_kv);
   const dsa::IndexerArgs a =
-      indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld, 0, d->n_q, d->n_q);
+      indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld, 0, d->n_q, d->n_q, pk);
   return hip_status(dsa::launch_indexer(a, d->n_q <= dsa::kIndexerDecodeMaxRows, (hipStream_t)stream),
                     "indexer launch");
 }
 
-int dsa_topk(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, void* stream) {
+int topk_impl(const dsa_dims* d, const dsa::PagedKV& pk, const float* scores, int64_t ld, int32_t* idx,
+              void* stream) {
   int st;
   if ((st = check_common(d)) != DSA_OK) return st;
   REQUIRE(scores && idx, DSA_ERR_INVALID_ARG, "null tensor pointer");
@@ -181,7 +226,8 @@ int dsa_topk(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, v
   REQUIRE(ld >= d->n_kv, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= n_kv (%d)", (long long)ld, d->n_kv);
   REQUIRE(d->n_kv <= dsa::topk_max_kv(), DSA_ERR_UNSUPPORTED, "n_kv (%d) exceeds the top-k limit %d", d->n_kv,
           dsa::topk_max_kv());
-  dsa::TopkArgs a;
+  dsa::TopkArgs a{};
+  a.pk = pk;
   a.scores = scores;
   a.idx = idx;
   a.ld = ld;
@@ -189,22 +235,18 @@ int dsa_topk(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, v
   a.idx_rows_b = d->n_q;
   a.B = d->batch;
   a.rows = d->n_q;
-  a.pos0 = d->q_pos0;
+  a.pos0 = pk.seq_lens ? 0 : d->q_pos0;
   a.S = d->n_kv;
   a.k = d->topk;
   return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "top-k launch");
 }
 
-size_t dsa_attn_workspace_size(const dsa_dims* d) {
-  if (check_common(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
-  return attn_partial_bytes(d, d->n_q);
-}
-
-static int validate_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                         float sm_scale, const uint16_t* out, const float* lse, bool idx_required) {
+int validate_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx, float sm_scale,
+                  const uint16_t* out, const float* lse, bool idx_required, bool dense) {
   int st;
   if ((st = check_common(d)) != DSA_OK) return st;
   if ((st = check_attn_dims(d)) != DSA_OK) return st;
+  if (dense && (st = check_dense_kv_size(d)) != DSA_OK) return st;
   REQUIRE(q && kv && out && (idx || !idx_required), DSA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16) && aligned(idx, 4) && aligned(lse, 4),
           DSA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned; idx and lse 4-byte aligned");
@@ -212,15 +254,17 @@ static int validate_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* k
   return DSA_OK;
 }
 
-int dsa_sparse_mla_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                        float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+int attn_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, const uint16_t* kv,
+              const int32_t* idx, float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+              void* stream) {
   int st;
-  if ((st = validate_attn(d, q, kv, idx, sm_scale, out, lse, true)) != DSA_OK) return st;
+  if ((st = validate_attn(d, q, kv, idx, sm_scale, out, lse, true, pk.page_table == nullptr)) != DSA_OK) return st;
   const size_t need = attn_partial_bytes(d, d->n_q);
   REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), DSA_ERR_WORKSPACE,
           "attention needs %zu workspace bytes (got %zu)", need, ws ? ws_bytes : (size_t)0);
   REQUIRE(need == 0 || aligned(ws, 16), DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  dsa::AttnArgs a;
+  dsa::AttnArgs a{};
+  a.pk = pk;
   a.q = q;
   a.kv = kv;
   a.idx = idx;
@@ -243,16 +287,13 @@ int dsa_sparse_mla_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv
   return hip_status(dsa::launch_sparse_mla(a, (hipStream_t)stream), "attention launch");
 }
 
-size_t dsa_forward_workspace_size(const dsa_dims* d) {
-  if (check_common(d) != DSA_OK || check_indexer_dims(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
-  return forward_layout(d).total;
-}
-
-int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
-                const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const uint16_t* kv, float sm_scale,
-                uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx, const float* q_scale,
+                 const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale, const uint16_t* q,
+                 const uint16_t* kv, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws,
+                 size_t ws_bytes, void* stream) {
   int st;
-  if ((st = validate_attn(d, q, kv, idx_out, sm_scale, out, lse, false)) != DSA_OK) return st;
+  if ((st = validate_attn(d, q, kv, idx_out, sm_scale, out, lse, false, pk.page_table == nullptr)) != DSA_OK)
+    return st;
   if ((st = check_indexer_dims(d)) != DSA_OK) return st;
   REQUIRE(q_idx && q_scale && w_idx && k_idx && k_scale, DSA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16), DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
@@ -270,13 +311,16 @@ int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, c
   float* sc = (float*)(wsb + L.scores_off);
   const bool decode_form = d->n_q <= dsa::kIndexerDecodeMaxRows;
   const int nsplit = attn_nsplit(d);
+  const int pos_base = pk.seq_lens ? 0 : d->q_pos0;
   for (int64_t i0 = 0; i0 < d->n_q; i0 += L.tc) {
     const int rows = (int)((d->n_q - i0) < L.tc ? (d->n_q - i0) : L.tc);
-    const dsa::IndexerArgs ia = indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, sc, d->n_kv, i0, rows, L.tc);
+    const dsa::IndexerArgs ia =
+        indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, sc, d->n_kv, i0, rows, L.tc, pk);
     hipError_t e = dsa::launch_indexer(ia, decode_form, s);
     if (e != hipSuccess) return hip_status(e, "indexer launch");
 
-    dsa::TopkArgs ta;
+    dsa::TopkArgs ta{};
+    ta.pk = pk;
     ta.scores = sc;
     ta.ld = d->n_kv;
     ta.sc_rows_b = L.tc;
@@ -284,13 +328,14 @@ int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, c
     ta.idx_rows_b = idx_out ? d->n_q : L.tc;
     ta.B = d->batch;
     ta.rows = rows;
-    ta.pos0 = d->q_pos0 + (int)i0;
+    ta.pos0 = pos_base + (int)i0;
     ta.S = d->n_kv;
     ta.k = d->topk;
     e = dsa::launch_topk(ta, s);
     if (e != hipSuccess) return hip_status(e, "top-k launch");
 
-    dsa::AttnArgs aa;
+    dsa::AttnArgs aa{};
+    aa.pk = pk;
     aa.q = q + i0 * d->heads * d->dim_qk;
     aa.kv = kv;
     aa.idx = ta.idx;
@@ -313,6 +358,95 @@ int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, c
     if (e != hipSuccess) return hip_status(e, "attention launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_indexer_scores(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
+                       const uint8_t* k_idx, const float* k_scale, float* scores, int64_t ld, void* stream) {
+  return indexer_impl(d, dsa::PagedKV{}, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld, stream);
+}
+
+int dsa_topk(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, void* stream) {
+  return topk_impl(d, dsa::PagedKV{}, scores, ld, idx, stream);
+}
+
+size_t dsa_attn_workspace_size(const dsa_dims* d) {
+  if (check_common(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
+  return attn_partial_bytes(d, d->n_q);
+}
+
+int dsa_sparse_mla_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                        float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_impl(d, dsa::PagedKV{}, q, kv, idx, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+size_t dsa_forward_workspace_size(const dsa_dims* d) {
+  if (check_common(d) != DSA_OK || check_indexer_dims(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
+  return forward_layout(d).total;
+}
+
+int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
+                const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const uint16_t* kv, float sm_scale,
+                uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(d, dsa::PagedKV{}, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_scale, out, lse, idx_out,
+                      ws, ws_bytes, stream);
+}
+
+#define PAGED_PROLOGUE                                  \
+  if (d == nullptr) return fail(DSA_ERR_INVALID_ARG, "dims is NULL"); \
+  const dsa_dims dd = paged_dims(d);                    \
+  dsa::PagedKV pk;                                      \
+  {                                                     \
+    const int st_ = check_paged(&dd, layout, &pk);      \
+    if (st_ != DSA_OK) return st_;                      \
+  }
+
+int dsa_indexer_scores_paged(const dsa_dims* d, const dsa_paged_kv* layout, const uint8_t* q_idx,
+                             const float* q_scale, const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale,
+                             float* scores, int64_t ld, void* stream) {
+  PAGED_PROLOGUE
+  return indexer_impl(&dd, pk, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld, stream);
+}
+
+int dsa_topk_paged(const dsa_dims* d, const dsa_paged_kv* layout, const float* scores, int64_t ld, int32_t* idx,
+                   void* stream) {
+  PAGED_PROLOGUE
+  return topk_impl(&dd, pk, scores, ld, idx, stream);
+}
+
+int dsa_sparse_mla_attn_paged(const dsa_dims* d, const dsa_paged_kv* layout, const uint16_t* q, const uint16_t* kv,
+                              const int32_t* idx, float sm_scale, uint16_t* out, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+  PAGED_PROLOGUE
+  return attn_impl(&dd, pk, q, kv, idx, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int dsa_forward_paged(const dsa_dims* d, const dsa_paged_kv* layout, const uint8_t* q_idx, const float* q_scale,
+                      const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale, const uint16_t* q,
+                      const uint16_t* kv, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  PAGED_PROLOGUE
+  return forward_impl(&dd, pk, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_scale, out, lse, idx_out, ws,
+                      ws_bytes, stream);
+}
+
+#undef PAGED_PROLOGUE
+
+int dsa_gather_stats(const dsa_dims* d, int32_t page_size, const int32_t* idx, int32_t* stats, void* stream) {
+  REQUIRE(d != nullptr, DSA_ERR_INVALID_ARG, "dims is NULL");
+  REQUIRE(d->batch >= 1 && d->n_q >= 1, DSA_ERR_INVALID_ARG, "batch and n_q must be >= 1 (got %d, %d)", d->batch,
+          d->n_q);
+  REQUIRE((int64_t)d->batch * d->n_q <= (1ll << 30), DSA_ERR_UNSUPPORTED, "batch * n_q too large");
+  REQUIRE(d->topk >= 1 && d->topk <= 2048, DSA_ERR_UNSUPPORTED, "topk must be in [1, 2048] (got %d)", d->topk);
+  REQUIRE(page_size >= 1, DSA_ERR_INVALID_ARG, "page_size must be >= 1 (got %d)", page_size);
+  REQUIRE(idx && stats, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(idx, 4) && aligned(stats, 4), DSA_ERR_INVALID_ARG, "misaligned idx/stats pointer");
+  return hip_status(dsa::launch_gather_stats(idx, stats, (int64_t)d->batch * d->n_q, d->topk, page_size,
+                                             (hipStream_t)stream),
+                    "gather stats launch");
 }
 
 }  // extern "C"

@@ -5,9 +5,43 @@
 
 namespace dsa {
 
+// Cache layout.  Dense (both pointers null): sequence b's token s is row
+// b * S + s of the caches and every sequence holds S tokens.  Otherwise
+// sequence b holds len(b) = clamp(seq_lens[b], n_q_total, S) tokens, its
+// query rows are its last n_q_total tokens, and with a page table its token
+// s is pool row page_table[b * max_pages + s / page_size] * page_size +
+// s % page_size (page entries clamped to [0, num_pages)).  Clamping keeps a
+// bad device-side value from addressing memory outside the buffers.
+struct PagedKV {
+  const int32_t* seq_lens;     // [B] or null
+  const int32_t* page_table;   // [B, max_pages] or null
+  int page_size, max_pages, num_pages;
+  int n_q_total;               // query rows per sequence (all chunks)
+};
+
+__device__ __forceinline__ int seq_len_of(const PagedKV& p, int b, int S) {
+  return p.seq_lens ? min(max(p.seq_lens[b], p.n_q_total), S) : S;
+}
+// Absolute position of a launch's row 0 of sequence b, given the launch's
+// pos0 (dense: the position itself; with seq_lens: the row offset within
+// the sequence's query rows).
+__device__ __forceinline__ int row_pos_base(const PagedKV& p, int b, int S, int pos0) {
+  return p.seq_lens ? seq_len_of(p, b, S) - p.n_q_total + pos0 : pos0;
+}
+// Physical page of logical page j of sequence b (paged layouts only).
+__device__ __forceinline__ int64_t page_of(const PagedKV& p, int b, int j) {
+  const int e = p.page_table[(int64_t)b * p.max_pages + min(j, p.max_pages - 1)];
+  return (int64_t)min(max(e, 0), p.num_pages - 1);
+}
+// Cache row of token s of sequence b.
+__device__ __forceinline__ int64_t cache_row(const PagedKV& p, int b, int S, int s) {
+  if (!p.page_table) return (int64_t)b * S + s;
+  return page_of(p, b, s / p.page_size) * p.page_size + s % p.page_size;
+}
+
 // A span of query rows: rows [0, rows) of each of B sequences, where row i
-// sits at absolute position pos0 + i.  Row-indexed tensors advance by
-// `qrows_b` rows from one sequence to the next.
+// sits at absolute position row_pos_base(pk, b, S, pos0) + i.  Row-indexed
+// tensors advance by `qrows_b` rows from one sequence to the next.
 struct IndexerArgs {
   const uint8_t* q_idx;   // [B, qrows_b, HI, dI] e4m3
   const float* q_scale;   // [B, qrows_b]
@@ -19,6 +53,7 @@ struct IndexerArgs {
   int64_t qrows_b;
   int64_t sc_rows_b;
   int B, rows, pos0, S, HI, dI;
+  PagedKV pk;             // k_idx / k_scale are pools when pk.page_table is set
 };
 
 struct TopkArgs {
@@ -28,6 +63,7 @@ struct TopkArgs {
   int64_t sc_rows_b;
   int64_t idx_rows_b;
   int B, rows, pos0, S, k;
+  PagedKV pk;             // only the lengths are used
 };
 
 struct AttnArgs {
@@ -42,6 +78,7 @@ struct AttnArgs {
   int64_t idx_rows_b;     // row stride between sequences for idx
   int B, rows, S, H, Dk, Dv, k, nsplit;
   float sm_scale;
+  PagedKV pk;             // kv is a pool when pk.page_table is set; idx holds token indices
 };
 
 // Kernel choice for the indexer: decode form (one row per wave, keys split
@@ -51,6 +88,10 @@ constexpr int kIndexerDecodeMaxRows = 4;
 hipError_t launch_indexer(const IndexerArgs& a, bool decode_form, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st);
+
+// Locality counters of rows of selected token indices ([rows, k], k <= 2048).
+hipError_t launch_gather_stats(const int32_t* idx, int32_t* stats, int64_t rows, int k, int page_size,
+                               hipStream_t st);
 
 // Shape support checks (true if the kernels are built for these dims).
 bool attn_dims_supported(int H, int Dk, int Dv);

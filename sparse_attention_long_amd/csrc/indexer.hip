@@ -51,45 +51,68 @@ __device__ __forceinline__ v8i load_q_tile(const IndexerArgs& a, int b, int i, i
   return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// Streaming form of the B operand for the key loops: `kb` is the sequence's
-// key base (uniform), `lane_off` = min(32*(lane/16), d_I-16) and `dmask`
-// says whether the lane's K bytes exist (d_I < 128 pads with zero).  Keys
-// at or beyond S read key S-1 instead; their results are never stored (each
-// score column depends only on its own key), so no zeroing is needed.
+// Streaming form of the B operand for the key loops.  A tile is 16 keys
+// sbase .. sbase+15 (sbase wave-uniform); lane l reads key sbase + l%16,
+// bytes [lane_off, lane_off + 32) where lane_off = min(32*(lane/16), d_I-16),
+// and `dmask` says whether the lane's K bytes exist (d_I < 128 pads with
+// zero).  Keys at or beyond S read key S-1 instead; their results are never
+// stored (each score column depends only on its own key), so no zeroing is
+// needed.
+//
+// Paged caches: a wave's key range [k_begin, k_end) spans at most 64 pages;
+// lane j holds the physical page of logical page k_begin/P + j, and a tile
+// (16-aligned, page sizes are multiples of 64) lies in one page, so its page
+// comes from one lane read.
 template <bool kFullD>
 struct KeyStream {
-  const uint8_t* kb;
+  const uint8_t* kb;      // dense: the sequence's keys; paged: the pool
+  const float* sb;        // the matching key scales
   int dI, smax, lane_off;
   bool lo_ok, hi_ok;
-  __device__ __forceinline__ void init(const IndexerArgs& a, int b, int lane) {
-    kb = a.k_idx + (int64_t)b * a.S * a.dI;
+  // paging
+  bool paged;
+  int psz, pfirst, pent;
+  __device__ __forceinline__ void init(const IndexerArgs& a, int b, int lane, int k_begin) {
+    paged = a.pk.page_table != nullptr;
+    kb = a.k_idx + (paged ? 0 : (int64_t)b * a.S * a.dI);
+    sb = a.k_scale + (paged ? 0 : (int64_t)b * a.S);
     dI = a.dI;
     smax = a.S - 1;
     const int off = 32 * (lane >> 4);
     lane_off = min(off, a.dI - 16);
     lo_ok = off < a.dI;
     hi_ok = off + 16 < a.dI;
+    psz = paged ? a.pk.page_size : 1;
+    pfirst = paged ? k_begin / psz : 0;
+    pent = paged ? (int)page_of(a.pk, b, pfirst + lane) : 0;
   }
-  __device__ __forceinline__ v8i load(int s) const {
+  // Cache row of key sbase + off (sbase wave-uniform, the tile in one page).
+  __device__ __forceinline__ int64_t row(int sbase, int off) const {
+    const int sb0 = min(sbase, smax);
+    const int s = min(sbase + off, smax);
+    if (!paged) return s;
+    const int pg = __builtin_amdgcn_readlane(pent, min(sb0 / psz - pfirst, 63));
+    return (int64_t)pg * psz + s % psz;
+  }
+  __device__ __forceinline__ v8i load(int sbase, int kl) const {
+    const uint8_t* p = kb + row(sbase, kl) * dI + lane_off;
     if constexpr (kFullD) {   // d_I = 128: every lane's 32 bytes exist
-      const uint32_t o = (uint32_t)(min(s, smax) * 128 + lane_off);
-      const u32x4 lo = *(const u32x4*)(kb + o);
-      const u32x4 hi = *(const u32x4*)(kb + o + 16);
+      const u32x4 lo = *(const u32x4*)p;
+      const u32x4 hi = *(const u32x4*)(p + 16);
       return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    const uint32_t o = (uint32_t)(min(s, smax) * dI + lane_off);
-    const u32x4 lo = *(const u32x4*)(kb + o);
-    const u32x4 hi = *(const u32x4*)(kb + o + (hi_ok ? 16 : 0));
+    const u32x4 lo = *(const u32x4*)p;
+    const u32x4 hi = *(const u32x4*)(p + (hi_ok ? 16 : 0));
     const u32x4 z = {0u, 0u, 0u, 0u};
     const u32x4 l = lo_ok ? lo : z, h = hi_ok ? hi : z;
     return (v8i){(int)l[0], (int)l[1], (int)l[2], (int)l[3], (int)h[0], (int)h[1], (int)h[2], (int)h[3]};
   }
+  // Scale of key sbase + off (zero past S).
+  __device__ __forceinline__ float scale(int sbase, int off) const {
+    const float v = sb[row(sbase, off)];
+    return sbase + off <= smax ? v : 0.f;
+  }
 };
-
-__device__ __forceinline__ float load_k_scale(const IndexerArgs& a, int b, int s) {
-  const float v = a.k_scale[(int64_t)b * a.S + min(s, a.S - 1)];
-  return s < a.S ? v : 0.f;
-}
 
 // Folded head weights w[t,j]*qs[t] for the 4 heads (per head tile) this lane
 // sees in the MFMA result: head 16*ht + 4*(lane/16) + r.
@@ -173,7 +196,8 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   const int i0 = qb * kPrefillRows + wave * kRowsPerWave;
   if (i0 >= a.rows) return;
   const int i_last = min(i0 + kRowsPerWave, a.rows) - 1;
-  const int np_last = min(a.pos0 + i_last + 1, a.S);
+  const int pb = row_pos_base(a.pk, b, a.S, a.pos0);
+  const int np_last = min(pb + i_last + 1, a.S);
   const int k_begin = kb * keys_per_wg;
   const int k_end = min(k_begin + keys_per_wg, np_last);
   if (k_begin >= k_end) return;
@@ -189,22 +213,22 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   // After the reduce-scatter, lane group g holds row i0 + g/2, tile g%2.
   const int g = lane >> 4;
   const int my_row = i0 + (g >> 1);
-  const int my_np = my_row < a.rows ? min(a.pos0 + my_row + 1, a.S) : 0;
+  const int my_np = my_row < a.rows ? min(pb + my_row + 1, a.S) : 0;
   float* my_out = a.scores + ((int64_t)b * a.sc_rows_b + min(my_row, a.rows - 1)) * a.ld;
   const v8i* qp[4] = {qa[0], qa[0], qa[1], qa[1]};
   const float(*wp[4])[4] = {wq[0], wq[0], wq[1], wq[1]};
 
   KeyStream<kFullD> ksr;
-  ksr.init(a, b, lane);
+  ksr.init(a, b, lane, k_begin);
   const int kl = lane & 15;
-  v8i kt0 = ksr.load(k_begin + kl);
-  v8i kt1 = ksr.load(k_begin + 16 + kl);
+  v8i kt0 = ksr.load(k_begin, kl);
+  v8i kt1 = ksr.load(k_begin + 16, kl);
   for (int s0 = k_begin; s0 < k_end; s0 += 32) {
     const int s = s0 + 16 * (g & 1) + kl;   // key this lane's result belongs to
-    const float ks = load_k_scale(a, b, s);
+    const float ks = ksr.scale(s0, 16 * (g & 1) + kl);
     // next step's tiles (past the block: harmless extra loads)
-    const v8i n0 = ksr.load(s0 + 32 + kl);
-    const v8i n1 = ksr.load(s0 + 48 + kl);
+    const v8i n0 = ksr.load(s0 + 32, kl);
+    const v8i n1 = ksr.load(s0 + 48, kl);
     const v8i* kp[4] = {&kt0, &kt1, &kt0, &kt1};
     float p[4];
     tile_partials<NHT>(qp, wp, kp, p);
@@ -261,7 +285,8 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   if (qb * kRows >= a.rows) return;
   const int blk_last = min(qb * kRows + kRows, a.rows) - 1;
   const int k_begin = kb * keys_per_wg;
-  const int k_end = min(k_begin + keys_per_wg, min(a.pos0 + blk_last + 1, a.S));
+  const int pb = row_pos_base(a.pk, b, a.S, a.pos0);
+  const int k_end = min(k_begin + keys_per_wg, min(pb + blk_last + 1, a.S));
   if (k_begin >= k_end) return;
   const int nsteps = (k_end - k_begin + 31) / 32;   // 32 keys per step, 8 steps per sub-block
   const int nsub = (nsteps + 7) / 8;
@@ -300,7 +325,7 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   const int g = lane >> 4;
   const int kl16 = lane & 15;
   const int my_row = i0 + (g >> 1);
-  const int my_np = min(my_row < a.rows ? min(a.pos0 + my_row + 1, a.S) : 0, k_end);
+  const int my_np = min(my_row < a.rows ? min(pb + my_row + 1, a.S) : 0, k_end);
   // Scores go out through a raw buffer store whose range covers this wave's
   // rows: a lane with nothing to store uses an offset past the range, which
   // the hardware drops, so the step loop has no divergent branch.
@@ -401,7 +426,7 @@ indexer_decode_kernel(IndexerArgs a) {
   const int wave = threadIdx.x >> 6;
   const int i = blockIdx.y;
   const int b = blockIdx.z;
-  const int np = min(a.pos0 + i + 1, a.S);
+  const int np = min(row_pos_base(a.pk, b, a.S, a.pos0) + i + 1, a.S);
   const int k_begin = (blockIdx.x * kDecodeWaves + wave) * kDecodeKeysPerWave;
   if (k_begin >= np) return;
   const int k_end = min(k_begin + kDecodeKeysPerWave, np);
@@ -416,17 +441,17 @@ indexer_decode_kernel(IndexerArgs a) {
   const float(*wp[4])[4] = {wq, wq, wq, wq};
 
   KeyStream<kFullD> ksr;
-  ksr.init(a, b, lane);
+  ksr.init(a, b, lane, k_begin);
   const int kl = lane & 15;
   v8i kt[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) kt[u] = ksr.load(k_begin + 16 * u + kl);
+  for (int u = 0; u < 4; ++u) kt[u] = ksr.load(k_begin + 16 * u, kl);
   for (int s0 = k_begin; s0 < k_end; s0 += 64) {
     const int s = s0 + lane;   // key whose score this lane ends up holding
-    const float ks = load_k_scale(a, b, s);
+    const float ks = ksr.scale(s0, lane);
     v8i nx[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) nx[u] = ksr.load(s0 + 64 + 16 * u + kl);
+    for (int u = 0; u < 4; ++u) nx[u] = ksr.load(s0 + 64 + 16 * u, kl);
     const v8i* kp[4] = {&kt[0], &kt[1], &kt[2], &kt[3]};
     float p[4];
     tile_partials<NHT>(qp, wp, kp, p);
@@ -442,13 +467,15 @@ bool lds_path_ok(const IndexerArgs& a) { return (2 * a.ld + (int64_t)a.S) * 4 < 
 
 template <int NHT, bool kFullD>
 hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
-  const int np_max = min(a.pos0 + a.rows, a.S);   // longest row
+  // longest row (with per-sequence lengths the host only knows the bound S)
+  const int np_max = a.pk.seq_lens ? a.S : min(a.pos0 + a.rows, a.S);
+  const bool lds_ok = kFullD && !a.pk.page_table && lds_path_ok(a);
   if (decode_form) {
     const int per_wg = kDecodeWaves * kDecodeKeysPerWave;
     dim3 grid((np_max + per_wg - 1) / per_wg, a.rows, a.B);
     hipLaunchKernelGGL((indexer_decode_kernel<NHT, kFullD>), grid, dim3(kDecodeWaves * kWave), 0, st, a);
   } else {
-    const int rows_per_wg = (kFullD && lds_path_ok(a)) ? kLdsRows : kPrefillRows;
+    const int rows_per_wg = lds_ok ? kLdsRows : kPrefillRows;
     const int nqb = (a.rows + rows_per_wg - 1) / rows_per_wg;
     // Large key blocks amortise the q loads (8 KB per row); smaller ones
     // keep at least ~512 workgroups busy.  Results do not depend on it.
@@ -461,7 +488,7 @@ hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
     const int nkb = (np_max + keys - 1) / keys;
     const int nkb8 = (nkb + 7) / 8;
     dim3 grid((unsigned)(8 * nqb * nkb8), a.B);
-    if (kFullD && lds_path_ok(a))
+    if (lds_ok)
       hipLaunchKernelGGL((indexer_prefill_lds_kernel<NHT, kLdsWaves>), grid, dim3(kLdsWaves * kWave), 0, st, a, keys, nqb);
     else
       hipLaunchKernelGGL((indexer_prefill_kernel<NHT, kFullD>), grid, dim3(kPrefillWaves * kWave), 0, st, a, keys, nqb);

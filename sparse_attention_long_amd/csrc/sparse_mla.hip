@@ -132,17 +132,20 @@ struct ChunkGather {
 };
 
 // Gather for the shapes whose part-A rows are exactly one wave instruction
-// (Dv = 512) with 4 waves: every copy takes the sequence's cache base as its
-// scalar address and a 32-bit per-lane byte offset (a sequence's latent cache
-// is below 4 GiB), so a row copy costs one lane read and one VALU op.  Wave w
-// copies rows j = 4*jj + w (jj < 8) of part A, whose piece swizzle is jj % 4,
-// and the part-B block of rows 8w .. 8w+7.
-template <int DK, int DV, int NW>
+// (Dv = 512) with 4 waves.  Wave w copies rows j = 4*jj + w (jj < 8) of part
+// A, whose piece swizzle is jj % 4, and the part-B block of rows 8w .. 8w+7.
+// Dense caches (K64 false): every copy takes the sequence's cache base as
+// its scalar address and a 32-bit per-lane byte offset (a sequence's latent
+// cache is below 4 GiB), so a row copy costs one lane read and one VALU op.
+// Page pools (K64 true) may exceed 4 GiB: a row copy reads the row's 64-bit
+// address into SGPRs (two lane reads) and part B uses 64-bit lane addresses.
+template <int DK, int DV, int NW, bool K64>
 struct RowGather {
   using C = Cfg<DK, DV, NW>;
   static_assert(C::kRowDma && NW == 4 && C::kDmaA == kChunk && C::kDmaB == NW, "row gather shape");
-  uint32_t off_a;   // lane j < 32: byte offset of chunk row j
-  uint32_t off_b;   // byte offset of this lane's part-B piece
+  uint32_t off_a;   // lane j < 32: byte offset of chunk row j (low half of it for K64)
+  uint32_t off_ah;  // K64: high half
+  uint64_t off_b;   // byte offset of this lane's part-B piece
   uint32_t lane16;  // 16 * lane
 
   // Chunk row whose index lane `lane` must supply for part B.
@@ -152,20 +155,31 @@ struct RowGather {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));   // keep the per-lane terms here, do not hoist them
     lane16 = 16u * (uint32_t)lane;
-    off_a = (uint32_t)max(ra, 0) * (uint32_t)(DK * 2);
+    const uint64_t oa = (uint64_t)max(ra, 0) * (uint64_t)(DK * 2);
+    off_a = (uint32_t)oa;
+    off_ah = (uint32_t)(oa >> 32);
     const int q = wave * kWave + lane;
     const int r = q / C::kPB, pp = q % C::kPB;
-    off_b = (uint32_t)max(rb, 0) * (uint32_t)(DK * 2) + 16u * (uint32_t)(C::kPA + (pp ^ (r & (C::kPB - 1))));
+    off_b = (uint64_t)max(rb, 0) * (uint64_t)(DK * 2) + 16u * (uint32_t)(C::kPA + (pp ^ (r & (C::kPB - 1))));
   }
   __device__ __forceinline__ void issue_all(uint16_t* tile, const uint16_t* kvb, int wave) const {
     const uint32_t t0 = lds_addr(tile);
 #pragma unroll
     for (int jj = 0; jj < C::kDmaA / NW; ++jj) {
       const int j = jj * NW + wave;
-      const uint32_t so = (uint32_t)__builtin_amdgcn_readlane((int)off_a, j);
-      dma_x4_s((lane16 ^ (16u * (uint32_t)(jj & 3))) + so, kvb, t0 + (uint32_t)j * (C::kRA * 16));
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)off_a, j);
+      if constexpr (K64) {
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)off_ah, j);
+        const uint8_t* rowp = (const uint8_t*)kvb + (((uint64_t)hi << 32) | lo);
+        dma_x4_s(lane16 ^ (16u * (uint32_t)(jj & 3)), rowp, t0 + (uint32_t)j * (C::kRA * 16));
+      } else {
+        dma_x4_s((lane16 ^ (16u * (uint32_t)(jj & 3))) + lo, kvb, t0 + (uint32_t)j * (C::kRA * 16));
+      }
     }
-    dma_x4_s(off_b, kvb, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
+    if constexpr (K64)
+      dma_x4((const uint8_t*)kvb + off_b, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
+    else
+      dma_x4_s((uint32_t)off_b, kvb, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
   }
 };
 
@@ -283,7 +297,7 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid,
   }
 }
 
-template <int DK, int DV, int NW>
+template <int DK, int DV, int NW, bool kPaged>
 __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   using C = Cfg<DK, DV, NW>;
   // Three LDS tiles as separate objects so the compiler can tell the tile
@@ -310,11 +324,15 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   const int nslots = max(0, min(per_split, a.k - slot0));
   const int nchunks = (nslots + kChunk - 1) / kChunk;
 
+  // Slot j holds the cache row of its token (-1 if the entry is padding or
+  // outside the sequence): a row of the sequence's cache, or of the pool.
+  const int slen = seq_len_of(a.pk, b, a.S);
   for (int j = threadIdx.x; j < nchunks * kChunk; j += C::kThreads) {
     int v = -1;
     if (j < nslots) {
       v = a.idx[((int64_t)b * a.idx_rows_b + i) * a.k + slot0 + j];
-      if (v < 0 || v >= a.S) v = -1;
+      if (v < 0 || v >= slen) v = -1;
+      else if (kPaged) v = (int)cache_row(a.pk, b, a.S, v);
     }
     sidx[j] = v;
   }
@@ -334,7 +352,7 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   wait_vm<0>();
   __syncthreads();
 
-  const uint16_t* kvb = a.kv + (int64_t)b * a.S * DK;
+  const uint16_t* kvb = kPaged ? a.kv : a.kv + (int64_t)b * a.S * DK;
   RowState<DK, DV, NW> rs;
   rs.m_ref = -INFINITY;
   rs.m_seen = -INFINITY;
@@ -348,7 +366,7 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto gather = [&](int c, uint16_t* fill, int ra, int rb) {
     if constexpr (C::kRowDma) {
-      RowGather<DK, DV, NW> g;
+      RowGather<DK, DV, NW, kPaged> g;
       g.init(ra, rb, wv);
       g.issue_all(fill, kvb, wv);
     } else {
@@ -358,7 +376,7 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
     }
   };
   auto rb_of = [&](int c) {
-    if constexpr (C::kRowDma) return sidx[c * kChunk + RowGather<DK, DV, NW>::row_b(wv, lane)];
+    if constexpr (C::kRowDma) return sidx[c * kChunk + RowGather<DK, DV, NW, kPaged>::row_b(wv, lane)];
     else return 0;
   };
   auto step = [&](int c, const uint16_t* cur, uint16_t* fill) {
@@ -471,7 +489,10 @@ __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
 template <int DK, int DV, int NW>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(a.B * a.rows * a.nsplit);
-  hipLaunchKernelGGL((sparse_mla_kernel<DK, DV, NW>), dim3(grid), dim3(NW * kWave), 0, st, a);
+  if (a.pk.page_table)
+    hipLaunchKernelGGL((sparse_mla_kernel<DK, DV, NW, true>), dim3(grid), dim3(NW * kWave), 0, st, a);
+  else
+    hipLaunchKernelGGL((sparse_mla_kernel<DK, DV, NW, false>), dim3(grid), dim3(NW * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3((unsigned)(a.B * a.rows * a.H)), dim3(DV / 4), 0, st, a);

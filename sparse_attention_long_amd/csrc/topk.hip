@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
   const int t = threadIdx.x;
   const int b = blockIdx.x / a.rows;
   const int i = blockIdx.x % a.rows;
-  const int n = min(a.pos0 + i + 1, a.S);
+  const int n = min(row_pos_base(a.pk, b, a.S, a.pos0) + i + 1, a.S);
   const int m = min(a.k, n);
   int32_t* out = a.idx + ((int64_t)b * a.idx_rows_b + i) * a.k;
   if (n <= a.k) {   // short row: every candidate is selected

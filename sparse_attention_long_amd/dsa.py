@@ -19,8 +19,9 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 # Every symbol include/dsa.h declares.
 EXPORTS = (
     "dsa_indexer_scores", "dsa_topk", "dsa_attn_workspace_size", "dsa_sparse_mla_attn",
-    "dsa_forward_workspace_size", "dsa_forward", "dsa_quantize_e4m3", "dsa_cache_append", "dsa_status_string",
-    "dsa_last_error", "dsa_version",
+    "dsa_forward_workspace_size", "dsa_forward", "dsa_quantize_e4m3", "dsa_cache_append",
+    "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged", "dsa_forward_paged",
+    "dsa_gather_stats", "dsa_status_string", "dsa_last_error", "dsa_version",
 )
 
 
@@ -40,6 +41,17 @@ class Dims(ctypes.Structure):
         vals = {n: getattr(wl, n) for n, _ in cls._fields_} if wl is not None else {}
         vals.update(kw)
         return cls(**vals)
+
+
+class PagedKV(ctypes.Structure):
+    """dsa_paged_kv: device pointers (ints) to seq_lens [B] and page_table
+    [B, max_pages] (0 for dense caches), and the page geometry."""
+    _fields_ = [("seq_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, seq_lens, page_table=None, page_size: int = 0, max_pages: int = 0, num_pages: int = 0):
+        return cls(_ptr(seq_lens), _ptr(page_table), page_size, max_pages, num_pages)
 
 
 _lib = None
@@ -63,11 +75,19 @@ def lib():
         L.dsa_forward.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.dsa_quantize_e4m3.argtypes = [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
         L.dsa_cache_append.argtypes = [D, _P, ctypes.c_int, _P, _P, _P, _P, _P]
+        K = ctypes.POINTER(PagedKV)
+        L.dsa_indexer_scores_paged.argtypes = [D, K, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]
+        L.dsa_topk_paged.argtypes = [D, K, _P, ctypes.c_int64, _P, _P]
+        L.dsa_sparse_mla_attn_paged.argtypes = [D, K, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dsa_forward_paged.argtypes = [D, K, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P,
+                                        ctypes.c_size_t, _P]
+        L.dsa_gather_stats.argtypes = [D, ctypes.c_int32, _P, _P, _P]
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.restype = ctypes.c_char_p
         for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_quantize_e4m3",
-                  "dsa_cache_append", "dsa_version"):
+                  "dsa_cache_append", "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged",
+                  "dsa_forward_paged", "dsa_gather_stats", "dsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,3 +168,33 @@ def dsa_quantize_e4m3(x, n_tokens: int, token_len: int, codes, scales, dtype=Non
 def dsa_cache_append(dims: Dims, k_new, k_idx, k_scale, kv_new=None, kv=None, k_dtype=None, stream=None):
     _check(lib().dsa_cache_append(ctypes.byref(dims), _ptr(k_new), _dtype_code(k_new, k_dtype), _ptr(kv_new),
                                   _ptr(k_idx), _ptr(k_scale), _ptr(kv), _stream(stream)))
+
+
+def dsa_indexer_scores_paged(dims: Dims, layout: PagedKV, q_idx, q_scale, w_idx, k_idx, k_scale, scores, ld: int,
+                             stream=None):
+    _check(lib().dsa_indexer_scores_paged(ctypes.byref(dims), ctypes.byref(layout), _ptr(q_idx), _ptr(q_scale),
+                                          _ptr(w_idx), _ptr(k_idx), _ptr(k_scale), _ptr(scores), int(ld),
+                                          _stream(stream)))
+
+
+def dsa_topk_paged(dims: Dims, layout: PagedKV, scores, ld: int, idx, stream=None):
+    _check(lib().dsa_topk_paged(ctypes.byref(dims), ctypes.byref(layout), _ptr(scores), int(ld), _ptr(idx),
+                                _stream(stream)))
+
+
+def dsa_sparse_mla_attn_paged(dims: Dims, layout: PagedKV, q, kv, idx, sm_scale: float, out, lse=None, ws=None,
+                              ws_bytes: int = 0, stream=None):
+    _check(lib().dsa_sparse_mla_attn_paged(ctypes.byref(dims), ctypes.byref(layout), _ptr(q), _ptr(kv), _ptr(idx),
+                                           float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), int(ws_bytes),
+                                           _stream(stream)))
+
+
+def dsa_forward_paged(dims: Dims, layout: PagedKV, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_scale: float,
+                      out, lse=None, idx_out=None, ws=None, ws_bytes: int = 0, stream=None):
+    _check(lib().dsa_forward_paged(ctypes.byref(dims), ctypes.byref(layout), _ptr(q_idx), _ptr(q_scale),
+                                   _ptr(w_idx), _ptr(k_idx), _ptr(k_scale), _ptr(q), _ptr(kv), float(sm_scale),
+                                   _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def dsa_gather_stats(dims: Dims, page_size: int, idx, stats, stream=None):
+    _check(lib().dsa_gather_stats(ctypes.byref(dims), int(page_size), _ptr(idx), _ptr(stats), _stream(stream)))

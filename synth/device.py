@@ -10,6 +10,7 @@ import numpy as np
 
 from . import gen
 from .workloads import Workload, _low_rank
+from .workloads import pool_rows as W_pool_rows
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa_synth.so")
@@ -75,4 +76,26 @@ def fill_inputs(wl: Workload, device="cuda"):
         _check(L.synth_fill_e4m3_tokens(wl.seed, gen.TID["k_idx"], 0, B * S, dI,
                                         t["k_idx"].data_ptr(), t["k_scale"].data_ptr(), st))
         _check(L.synth_fill_bf16(wl.seed, gen.TID["kv"], 0, B * S * Dk, 0, t["kv"].data_ptr(), st))
+    return t
+
+
+def fill_paged(wl: Workload, layout, device="cuda"):
+    """Inputs of `wl` with the caches moved into page pools per `layout`
+    (synth.workloads.PagedLayout): the dict of fill_inputs with k_idx,
+    k_scale and kv replaced by pools [num_pages * page_size, ...] (slots of
+    unused pages and past a sequence's capacity hold zeros), plus the device
+    int32 tensors seq_lens [B] and page_table [B, max_pages]."""
+    import torch
+    t = fill_inputs(wl, device)
+    B, S, P = wl.batch, wl.n_kv, layout.page_size
+    rows = layout.num_pages * P
+    slots = torch.from_numpy(np.stack([W_pool_rows(layout, b, np.arange(S)) for b in range(B)])).to(device)
+    for name, tail in (("k_idx", (wl.idx_dim,)), ("k_scale", ()), ("kv", (wl.dim_qk,))):
+        dense = t[name]
+        pool = torch.zeros((rows,) + tail, dtype=dense.dtype, device=device)
+        pool.index_copy_(0, slots.reshape(-1), dense.reshape((B * S,) + tail))
+        t[name] = pool
+        del dense
+    t["seq_lens"] = torch.tensor(layout.seq_lens, dtype=torch.int32, device=device)
+    t["page_table"] = torch.from_numpy(layout.table).to(device)
     return t

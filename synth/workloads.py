@@ -188,3 +188,42 @@ def host_inputs(wl: Workload):
         "q_idx": np.stack(qc), "q_scale": np.stack(qs), "w_idx": np.stack(w),
         "k_idx": np.stack(kc), "k_scale": np.stack(ks), "q": np.stack(q), "kv": np.stack(kv),
     }
+
+
+# ----------------------------------------------------------------- paged / variable-length layouts
+@dataclasses.dataclass(frozen=True)
+class PagedLayout:
+    """Per-sequence lengths and a page placement for workload `base`:
+    sequence b holds seq_lens[b] tokens; its logical page j lives in
+    physical page table[b, j] of a pool of num_pages pages."""
+    page_size: int
+    seq_lens: tuple
+    table: np.ndarray      # int32 [B, max_pages]
+    num_pages: int
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.table.shape[1])
+
+
+def paged_layout(wl: Workload, page_size: int, min_len: int | None = None, spare_pages: int = 3,
+                 full: bool = False) -> PagedLayout:
+    """Seeded layout: lengths uniform in [min_len, n_kv] (all n_kv if `full`),
+    at least n_q; every sequence owns ceil(n_kv / page_size) pages, placed at
+    random in a pool that also holds `spare_pages` unused pages."""
+    rs = np.random.RandomState(wl.seed + 7919)
+    lo = max(wl.n_q, min_len if min_len is not None else wl.n_q)
+    if full:
+        lens = [wl.n_kv] * wl.batch
+    else:
+        lens = [int(x) for x in rs.randint(lo, wl.n_kv + 1, size=wl.batch)]
+    max_pages = (wl.n_kv + page_size - 1) // page_size
+    num_pages = wl.batch * max_pages + spare_pages
+    table = rs.permutation(num_pages)[:wl.batch * max_pages].reshape(wl.batch, max_pages).astype(np.int32)
+    return PagedLayout(page_size, tuple(lens), table, num_pages)
+
+
+def pool_rows(layout: PagedLayout, b: int, s) -> np.ndarray:
+    """Pool rows of tokens s (array) of sequence b."""
+    s = np.asarray(s, dtype=np.int64)
+    return layout.table[b, s // layout.page_size].astype(np.int64) * layout.page_size + s % layout.page_size

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert dsa.dsa_version() == 101
+    assert dsa.dsa_version() == 102
     L = dsa.lib()
     assert L.dsa_status_string(0) == b"ok"
     assert L.dsa_status_string(3) == b"workspace too small"
@@ -98,7 +98,8 @@ def test_attention_validation_and_workspace():
         dsa.dsa_sparse_mla_attn(_dims(n_q=1, n_kv=limit + 1, q_pos0=limit, topk=2048), FAKE, FAKE, FAKE, 0.1, FAKE,
                                 ws=FAKE, ws_bytes=1 << 30, stream=0)
     assert e.value.status == dsa.dsa.ERR_UNSUPPORTED and "4 GiB" in str(e.value)
-    assert dsa.dsa_attn_workspace_size(_dims(n_q=1, n_kv=limit + 1, q_pos0=limit, topk=2048)) == 0
+    # the workspace does not depend on the cache layout (page pools have no such limit)
+    assert dsa.dsa_attn_workspace_size(_dims(n_q=1, n_kv=limit + 1, q_pos0=limit, topk=2048)) > 0
 
 
 def test_forward_workspace_plan():
@@ -134,3 +135,56 @@ def test_cache_append_validation():
     with pytest.raises(dsa.DSAError) as e:
         dsa.dsa.dsa_cache_append(_dims(n_q=1, n_kv=8, q_pos0=7, idx_dim=6), FAKE, FAKE, FAKE, k_dtype=1, stream=0)
     assert e.value.status == dsa.dsa.ERR_UNSUPPORTED
+
+
+def _layout(**kw):
+    base = dict(seq_lens=FAKE, page_table=FAKE + 4096, page_size=64, max_pages=4, num_pages=16)
+    base.update(kw)
+    return dsa.dsa.PagedKV.of(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_lens=None), dsa.dsa.ERR_INVALID_ARG),
+    (dict(seq_lens=FAKE + 2), dsa.dsa.ERR_INVALID_ARG),          # misaligned
+    (dict(page_size=32), dsa.dsa.ERR_UNSUPPORTED),               # not a multiple of 64
+    (dict(page_size=0), dsa.dsa.ERR_UNSUPPORTED),
+    (dict(max_pages=1), dsa.dsa.ERR_INVALID_ARG),                # 1 x 64 < n_kv = 200
+    (dict(num_pages=0), dsa.dsa.ERR_UNSUPPORTED),
+    (dict(num_pages=1 << 25, page_size=64), dsa.dsa.ERR_UNSUPPORTED),   # pool of 2^31 rows
+])
+def test_paged_layout_validation(kw, status):
+    d = _dims(batch=2, n_q=1, n_kv=200, topk=16)
+    lay = _layout(**kw)
+    for call in (lambda: dsa.dsa.dsa_indexer_scores_paged(d, lay, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 200, stream=0),
+                 lambda: dsa.dsa.dsa_topk_paged(d, lay, FAKE, 200, FAKE, stream=0),
+                 lambda: dsa.dsa.dsa_sparse_mla_attn_paged(d, lay, FAKE, FAKE, FAKE, 0.1, FAKE, ws=FAKE,
+                                                           ws_bytes=1 << 30, stream=0),
+                 lambda: dsa.dsa.dsa_forward_paged(d, lay, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE,
+                                                   ws=FAKE, ws_bytes=1 << 30, stream=0)):
+        with pytest.raises(dsa.DSAError) as e:
+            call()
+        assert e.value.status == status
+
+
+def test_paged_calls_keep_the_other_checks():
+    d = _dims(batch=2, n_q=1, n_kv=200, topk=16)
+    with pytest.raises(dsa.DSAError) as e:   # ld below n_kv
+        dsa.dsa.dsa_indexer_scores_paged(d, _layout(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 199, stream=0)
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+    with pytest.raises(dsa.DSAError) as e:   # forward workspace too small
+        dsa.dsa.dsa_forward_paged(d, _layout(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE,
+                                  ws=FAKE, ws_bytes=16, stream=0)
+    assert e.value.status == dsa.dsa.ERR_WORKSPACE
+    # q_pos0 plays no part in the paged calls (positions come from seq_lens)
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa.dsa_topk_paged(_dims(batch=2, n_q=1, n_kv=200, topk=16, q_pos0=5000), _layout(), FAKE, 199, FAKE,
+                               stream=0)
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG and "ld" in str(e.value)
+
+
+def test_gather_stats_validation():
+    for kw, ps, status in ((dict(), 0, dsa.dsa.ERR_INVALID_ARG), (dict(topk=4096), 64, dsa.dsa.ERR_UNSUPPORTED),
+                           (dict(n_q=0), 64, dsa.dsa.ERR_INVALID_ARG)):
+        with pytest.raises(dsa.DSAError) as e:
+            dsa.dsa.dsa_gather_stats(_dims(**kw), ps, FAKE, FAKE, stream=0)
+        assert e.value.status == status

@@ -330,3 +330,64 @@ def test_quantize_round_trip_error_bound():
     a = np.abs(x.astype(np.float64) / scales[:, None])
     ulp = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
     assert np.all(np.abs(back - x) <= 0.5 * ulp * scales[:, None] * (1 + 1e-6) + 1e-30)
+
+
+# ------------------------------------------------------------------ paged / variable-length caches
+def test_gather_stats_worked_examples(golden_dir):
+    for line in open(f"{golden_dir}/gather_stats_worked.txt"):
+        if line.startswith("#") or not line.strip():
+            continue
+        ps, sel, want = (x.split() for x in line.split("|"))
+        got = O.gather_stats([int(v) for v in sel], int(ps[0]))
+        assert got == tuple(int(v) for v in want), (line, got)
+
+
+def test_gather_stats_matches_a_walk_over_the_row():
+    # An independent count: walk the ascending selection once, opening a run
+    # whenever the index does not follow its predecessor and counting hits per
+    # page in a dict.
+    rs = np.random.RandomState(31)
+    for _ in range(200):
+        n = int(rs.randint(0, 3000))
+        m = int(rs.randint(0, min(n, 300) + 1))
+        sel = np.sort(rs.choice(n, size=m, replace=False)) if m else np.zeros(0, np.int64)
+        ps = int(rs.choice([16, 64, 128]))
+        runs, prev, hits = 0, None, {}
+        for s in sel:
+            if prev is None or s != prev + 1:
+                runs += 1
+            prev = s
+            hits[s // ps] = hits.get(s // ps, 0) + 1
+        want = (len(hits), runs, max(hits.values()) if hits else 0)
+        padded = np.concatenate([sel, -np.ones(5, np.int64)])
+        assert O.gather_stats(padded, ps) == want
+
+
+def test_paged_gather_inverts_the_page_scatter():
+    # Build a pool by scattering each sequence's pages to random slots; the
+    # gather through the page table must give the dense tokens back, and an
+    # identity table must be a plain slice.
+    rs = np.random.RandomState(32)
+    P, B, S = 16, 3, 80
+    npages = (S + P - 1) // P
+    dense = rs.randn(B, npages * P, 5)
+    table = rs.permutation(B * npages + 4)[:B * npages].reshape(B, npages)
+    pool = np.full((table.max() + 1) * P, np.nan)[:, None] * np.ones((1, 5))
+    for b in range(B):
+        for j in range(npages):
+            pool[table[b, j] * P:(table[b, j] + 1) * P] = dense[b, j * P:(j + 1) * P]
+    for b in range(B):
+        n = int(rs.randint(1, S + 1))
+        assert np.array_equal(O.paged_gather(pool, table[b], P, n), dense[b, :n])
+    flat = dense.reshape(-1, 5)
+    assert np.array_equal(O.paged_gather(flat, np.arange(npages) + npages, P, S), flat[npages * P:npages * P + S])
+
+
+def test_varlen_rows_are_the_sequence_tail():
+    # Decode sees itself as the last cached token; n_q new tokens are the last
+    # n_q positions, and each row's candidate count is its position + 1.
+    assert O.varlen_positions(100, 1) == [99]
+    assert O.varlen_positions(7, 3) == [4, 5, 6]
+    for L, n_q in ((5, 5), (130, 4)):
+        pos = O.varlen_positions(L, n_q)
+        assert [O.n_candidates(p, L) for p in pos] == list(range(L - n_q + 1, L + 1))
