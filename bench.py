@@ -198,6 +198,79 @@ def time_quantize(torch, dsa, wl, stream, reps=5):
     return res
 
 
+def time_decode_paged(torch, dsa, stream, reps=10, warmup=2):
+    """The decode step over paged, variable-length caches: 64 sequences with
+    lengths uniform in [64K, 128K] tokens, 64-token pages placed at random in
+    one pool.  Times dsa_forward_paged and the three paged calls separately,
+    and reports the selections' locality counters (dsa_gather_stats)."""
+    from synth import workloads as W
+    from synth.device import fill_paged
+    D = dsa.dsa
+    wl = W.WORKLOADS["dec64"]
+    P = 64
+    lay = W.paged_layout(wl, P, min_len=wl.n_kv // 2)
+    d = fill_paged(wl, lay)
+    pk = D.PagedKV.of(d["seq_lens"], d["page_table"], P, lay.max_pages, lay.num_pages)
+    dims = D.Dims.of(wl)
+    B, S, k = wl.batch, wl.n_kv, wl.topk
+    out = torch.empty((B, 1, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    fws = D.dsa_forward_workspace_size(dims)
+    ws = torch.empty(fws, dtype=torch.uint8, device="cuda")
+    sc = torch.empty((B, 1, S), dtype=torch.float32, device="cuda")
+    nws = D.dsa_attn_workspace_size(dims)
+    aws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    stats = torch.empty((B, 1, 3), dtype=torch.int32, device="cuda")
+    st = stream.cuda_stream
+    args = (d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"])
+
+    def fwd():
+        D.dsa_forward_paged(dims, pk, *args, d["q"], d["kv"], wl.sm_scale, out, None, idx, ws, fws, stream=st)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    e0 = t.event()
+    for _ in range(reps):
+        fwd()
+    e1 = t.event()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / reps
+    tot = {"indexer": 0.0, "topk": 0.0, "attention": 0.0, "gather_stats": 0.0}
+    for _ in range(reps):
+        ev = [t.event()]
+        D.dsa_indexer_scores_paged(dims, pk, *args, sc, S, stream=st)
+        ev.append(t.event())
+        D.dsa_topk_paged(dims, pk, sc, S, idx, stream=st)
+        ev.append(t.event())
+        D.dsa_sparse_mla_attn_paged(dims, pk, d["q"], d["kv"], idx, wl.sm_scale, out, None, aws, nws, stream=st)
+        ev.append(t.event())
+        D.dsa_gather_stats(dims, P, idx, stats, stream=st)
+        ev.append(t.event())
+        torch.cuda.synchronize()
+        for j, name in enumerate(tot):
+            tot[name] += ev[j].elapsed_time(ev[j + 1]) / reps
+    lens = np.array(lay.seq_lens, dtype=np.int64)
+    sel = np.minimum(k, lens)
+    idx_bytes = int((lens * (wl.idx_dim + 4)).sum() + B * wl.idx_heads * (wl.idx_dim + 2) + 4 * B
+                    + 4 * lens.sum())
+    topk_b = int(4 * lens.sum() + 4 * B * k)
+    mla_bytes = int((sel * wl.dim_qk * 2).sum() + B * wl.heads * wl.dim_qk * 2 + B * wl.heads * wl.dim_v * 2)
+    step_bytes = idx_bytes + topk_b + mla_bytes
+    st_np = stats.cpu().numpy().reshape(B, 3).astype(np.float64)
+    res = {"workload": "dec64 paged: 64 x [64K, 128K] tokens, 64-token pages", "page_size": P,
+           "mean_seq_len": float(lens.mean()), "ms_per_step": step_ms,
+           "GB_per_s": step_bytes / (step_ms / 1e3) / 1e9, "stages_ms": tot,
+           "indexer_GB_per_s": idx_bytes / (tot["indexer"] / 1e3) / 1e9,
+           "mla_gather_GB_per_s": mla_bytes / (tot["attention"] / 1e3) / 1e9,
+           "algorithmic_bytes_per_step": step_bytes,
+           "selection_locality": {"mean_pages": float(st_np[:, 0].mean()), "mean_runs": float(st_np[:, 1].mean()),
+                                  "mean_max_hits_per_page": float(st_np[:, 2].mean())}}
+    del d
+    return res
+
+
 def cpu_baseline(wl, n_rows):
     """The CPU oracle (unchanged) on a stratified sample of query rows:
     rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
@@ -322,6 +395,13 @@ def main():
         del dd
         torch.cuda.empty_cache()
 
+    decode_paged = None
+    if not args.no_decode:
+        log("[bench] paged variable-length decode (dec64 layout, 64-token pages)")
+        decode_paged = time_decode_paged(torch, dsa, stream)
+        log(f"[bench] decode paged {decode_paged}")
+        torch.cuda.empty_cache()
+
     quant = None
     if not args.no_decode:
         log("[bench] FP8 quantisation of the index keys and of 16384 query tokens")
@@ -343,7 +423,8 @@ def main():
                    "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim, "heads": wl.heads, "dim_qk": wl.dim_qk,
                    "dim_v": wl.dim_v},
         "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
-        "topk_GB_per_s": topk_gbs, "roofline": roof, "decode": decode, "quantize": quant, "cpu_baseline": cpu,
+        "topk_GB_per_s": topk_gbs, "roofline": roof, "decode": decode, "decode_paged": decode_paged,
+        "quantize": quant, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
