@@ -75,6 +75,28 @@ def time_forward(torch, wl, d, dsa, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def time_forward_kl(torch, wl, d, dsa, steps, warmup, stream):
+    """The sparse-stage training forward (dsa_forward_kl: the forward plus the
+    indexer KL of Eq. (4) per row), whole-workload ms per step."""
+    dims, out, lse, ws, nws = alloc_forward(torch, wl, dsa)
+    kl = torch.empty((wl.batch, wl.n_q), dtype=torch.float32, device="cuda")
+
+    def step():
+        dsa.dsa.dsa_forward_kl(dims, None, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], d["q"],
+                               d["kv"], wl.sm_scale, out, lse, None, kl, ws, nws, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    e0 = t.event()
+    for _ in range(steps):
+        step()
+    e1 = t.event()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, float(kl.double().mean().item())
+
+
 def time_stages(torch, wl, d, dsa, reps, stream):
     """The forward's chunk loop through the three separate calls (bit-identical
     launches), with events between stages: per-kernel average durations."""
@@ -368,6 +390,17 @@ def main():
     roof["traffic"] = profiled_traffic(dom, wl.name)
     roof["launches"] = launches
     roof["avg_launch_us"] = stages[dom] * 1e3 / max(launches, 1)
+
+    train = None
+    if not args.no_decode:
+        log("[bench] sparse-stage training forward (dsa_forward_kl)")
+        kms, kl_mean = time_forward_kl(torch, wl, d, dsa, max(1, min(args.steps, 2)), 1, stream)
+        kl_ms = kms - ms
+        qk_flop = 2.0 * wl.selected_pairs() * wl.heads * wl.dim_qk
+        train = {"ms_per_step": kms, "query_tokens_per_s": wl.batch * wl.n_q / (kms / 1e3),
+                 "kl_increment_ms": kl_ms, "kl_qk_tflops": qk_flop / (kl_ms / 1e3) / 1e12 if kl_ms > 0 else None,
+                 "mean_kl": kl_mean}
+        log(f"[bench] training forward {train}")
     del d
     torch.cuda.empty_cache()
 
@@ -423,7 +456,8 @@ def main():
                    "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim, "heads": wl.heads, "dim_qk": wl.dim_qk,
                    "dim_v": wl.dim_v},
         "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
-        "topk_GB_per_s": topk_gbs, "roofline": roof, "decode": decode, "decode_paged": decode_paged,
+        "topk_GB_per_s": topk_gbs, "roofline": roof, "train_forward_kl": train, "decode": decode,
+        "decode_paged": decode_paged,
         "quantize": quant, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

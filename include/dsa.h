@@ -243,6 +243,32 @@ int dsa_forward_paged(const dsa_dims* dims, const dsa_paged_kv* layout, const ui
  */
 int dsa_gather_stats(const dsa_dims* dims, int32_t page_size, const int32_t* idx, int32_t* stats, void* stream);
 
+/*
+ * Forward indexer KL on the selected set (page "6.2 DSA Continued
+ * Pre-Training: Warm-up and Sparse Stages", sparse stage; the analysis page,
+ * Sec. 1.1 Eq. (4)): for every query row t with selection S_t (idx),
+ *   P_s   = sum_h exp(sm_scale * q[t,h] . kv[s] - lse[t,h])   (the attention
+ *           weights of all heads over S_t; lse from dsa_sparse_mla_attn)
+ *   p_s   = P_s / sum_{s' in S_t} P_s'                         (L1 normalised)
+ *   kl[t] = sum_{s in S_t} p_s (ln p_s - ln softmax_{S_t}(I[t,:])_s)
+ * with I[t,s] = scores[b, i, s] (the index scores).  kl is [B, n_q] f32; a
+ * row with an empty selection gets 0.  layout may be NULL (dense caches, as
+ * in dsa_sparse_mla_attn) or a paged / variable-length layout (as in the
+ * _paged calls; idx holds token indices).  The weights are recomputed from
+ * q and kv on bf16 MFMA with fp32 accumulation; sums are fp32.
+ */
+int dsa_indexer_kl(const dsa_dims* dims, const dsa_paged_kv* layout, const uint16_t* q, const uint16_t* kv,
+                   const int32_t* idx, const float* lse, const float* scores, int64_t ld, float sm_scale,
+                   float* kl, void* stream);
+/* dsa_forward (layout NULL) or dsa_forward_paged, plus kl [B, n_q] as in
+ * dsa_indexer_kl for each chunk's selection and scores (the training forward
+ * of the sparse stage).  lse and kl are required.  Equal, bit for bit, to the
+ * forward followed by dsa_indexer_kl on its selection and scores. */
+int dsa_forward_kl(const dsa_dims* dims, const dsa_paged_kv* layout, const uint8_t* q_idx, const float* q_scale,
+                   const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale, const uint16_t* q,
+                   const uint16_t* kv, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, float* kl,
+                   void* ws, size_t ws_bytes, void* stream);
+
 /* Status text, thread-local last error message, ABI version (major*100+minor). */
 const char* dsa_status_string(int status);
 const char* dsa_last_error(void);

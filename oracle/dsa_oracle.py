@@ -247,3 +247,31 @@ def gather_stats(sel, page_size: int):
     pages, hits = np.unique(s // page_size, return_counts=True)
     runs = 1 + int(np.count_nonzero(np.diff(s) != 1))
     return int(pages.size), runs, int(hits.max())
+
+
+# ----------------------------------------------------------------- indexer KL on the selected set
+# Page "6.2 DSA Continued Pre-Training: Warm-up and Sparse Stages" (Stage 2)
+# and the analysis page, Sec. 1.1 Eq. (4): the indexer is trained towards
+# the main attention on the selected set.  The target p sums the attention
+# weights of all heads and L1-normalises along the sequence; the loss of a
+# query is KL(p_{t,S_t} || Softmax(I_{t,S_t})).
+def indexer_kl_row(q_t, kv, sel, scores, sm_scale: float, dim_v: int):
+    """KL divergence of one query row.
+
+    q_t [H, Dk], kv [S, Dk] latent rows, sel: selected token indices (entries
+    < 0 skipped), scores: the row's index scores I[t, s] (indexable by s).
+    p_s = sum_h P[h, s] / sum_{h, s'} P[h, s'] with P the sparse attention
+    weights of Eq. (19); q = softmax of I over the selected set.  Returns
+    sum_s p_s (ln p_s - ln q_s) in float64 (0 for an empty selection)."""
+    s = np.asarray(sel)
+    s = s[s >= 0]
+    if s.size == 0:
+        return 0.0
+    _, _, P = sparse_mla_row(q_t, kv, s, sm_scale, dim_v, return_weights=True)   # [H, m]
+    agg = P.sum(axis=0)
+    p = agg / agg.sum()
+    i_sel = np.asarray(scores, dtype=np.float64)[s]
+    i_max = i_sel.max()
+    log_q = i_sel - (i_max + np.log(np.exp(i_sel - i_max).sum()))
+    nz = p > 0
+    return float((p[nz] * (np.log(p[nz]) - log_q[nz])).sum())

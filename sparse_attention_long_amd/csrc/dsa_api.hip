@@ -181,7 +181,7 @@ dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const flo
 
 extern "C" {
 
-int dsa_version(void) { return 102; }
+int dsa_version(void) { return 103; }
 
 const char* dsa_status_string(int status) {
   switch (status) {
@@ -290,8 +290,10 @@ int attn_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, cons
 int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx, const float* q_scale,
                  const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale, const uint16_t* q,
                  const uint16_t* kv, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 size_t ws_bytes, void* stream, float* kl = nullptr) {
   int st;
+  REQUIRE(kl == nullptr || (lse != nullptr && aligned(kl, 4)), DSA_ERR_INVALID_ARG,
+          "the indexer KL needs lse (the attention's log-sum-exp) and a 4-byte aligned kl buffer");
   if ((st = validate_attn(d, q, kv, idx_out, sm_scale, out, lse, false, pk.page_table == nullptr)) != DSA_OK)
     return st;
   if ((st = check_indexer_dims(d)) != DSA_OK) return st;
@@ -356,8 +358,54 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     aa.sm_scale = sm_scale;
     e = dsa::launch_sparse_mla(aa, s);
     if (e != hipSuccess) return hip_status(e, "attention launch");
+    if (kl) {
+      dsa::KlArgs ka{};
+      ka.at = aa;
+      ka.scores = sc;
+      ka.ld = d->n_kv;
+      ka.sc_rows_b = L.tc;
+      ka.kl = kl + i0;
+      e = dsa::launch_indexer_kl(ka, s);
+      if (e != hipSuccess) return hip_status(e, "indexer KL launch");
+    }
   }
   return ok();
+}
+
+int kl_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+            const float* lse, const float* scores, int64_t ld, float sm_scale, float* kl, void* stream) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  if ((st = check_attn_dims(d)) != DSA_OK) return st;
+  if (pk.page_table == nullptr && (st = check_dense_kv_size(d)) != DSA_OK) return st;
+  REQUIRE(q && kv && idx && lse && scores && kl, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(idx, 4) && aligned(lse, 4) && aligned(scores, 4) &&
+              aligned(kl, 4),
+          DSA_ERR_INVALID_ARG, "q and kv must be 16-byte aligned; idx, lse, scores and kl 4-byte aligned");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  REQUIRE(ld >= d->n_kv, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= n_kv (%d)", (long long)ld, d->n_kv);
+  dsa::KlArgs ka{};
+  ka.at.pk = pk;
+  ka.at.q = q;
+  ka.at.kv = kv;
+  ka.at.idx = idx;
+  ka.at.lse = const_cast<float*>(lse);
+  ka.at.qrows_b = d->n_q;
+  ka.at.idx_rows_b = d->n_q;
+  ka.at.B = d->batch;
+  ka.at.rows = d->n_q;
+  ka.at.S = d->n_kv;
+  ka.at.H = d->heads;
+  ka.at.Dk = d->dim_qk;
+  ka.at.Dv = d->dim_v;
+  ka.at.k = d->topk;
+  ka.at.nsplit = 1;
+  ka.at.sm_scale = sm_scale;
+  ka.scores = scores;
+  ka.ld = ld;
+  ka.sc_rows_b = d->n_q;
+  ka.kl = kl;
+  return hip_status(dsa::launch_indexer_kl(ka, (hipStream_t)stream), "indexer KL launch");
 }
 
 }  // namespace
@@ -433,6 +481,35 @@ int dsa_forward_paged(const dsa_dims* d, const dsa_paged_kv* layout, const uint8
                       ws_bytes, stream);
 }
 
+// Layout-optional calls: a NULL layout means dense caches.
+#define LAYOUT_PROLOGUE                                 \
+  if (d == nullptr) return fail(DSA_ERR_INVALID_ARG, "dims is NULL"); \
+  dsa::PagedKV pk{};                                    \
+  dsa_dims dd = *d;                                     \
+  if (layout) {                                         \
+    dd = paged_dims(d);                                 \
+    const int st_ = check_paged(&dd, layout, &pk);      \
+    if (st_ != DSA_OK) return st_;                      \
+  }
+
+int dsa_indexer_kl(const dsa_dims* d, const dsa_paged_kv* layout, const uint16_t* q, const uint16_t* kv,
+                   const int32_t* idx, const float* lse, const float* scores, int64_t ld, float sm_scale, float* kl,
+                   void* stream) {
+  LAYOUT_PROLOGUE
+  return kl_impl(&dd, pk, q, kv, idx, lse, scores, ld, sm_scale, kl, stream);
+}
+
+int dsa_forward_kl(const dsa_dims* d, const dsa_paged_kv* layout, const uint8_t* q_idx, const float* q_scale,
+                   const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale, const uint16_t* q,
+                   const uint16_t* kv, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, float* kl,
+                   void* ws, size_t ws_bytes, void* stream) {
+  LAYOUT_PROLOGUE
+  REQUIRE(kl != nullptr && lse != nullptr, DSA_ERR_INVALID_ARG, "kl and lse are required");
+  return forward_impl(&dd, pk, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_scale, out, lse, idx_out, ws,
+                      ws_bytes, stream, kl);
+}
+
+#undef LAYOUT_PROLOGUE
 #undef PAGED_PROLOGUE
 
 int dsa_gather_stats(const dsa_dims* d, int32_t page_size, const int32_t* idx, int32_t* stats, void* stream) {

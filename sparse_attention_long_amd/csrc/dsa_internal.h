@@ -88,6 +88,15 @@ constexpr int kIndexerDecodeMaxRows = 4;
 hipError_t launch_indexer(const IndexerArgs& a, bool decode_form, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st);
+// Indexer KL of each row over its selection: `at` as for the attention, with
+// at.lse the attention's log-sum-exp (input), at.out unused.
+struct KlArgs {
+  AttnArgs at;
+  const float* scores;    // [B, sc_rows_b, ld] index scores of the rows
+  int64_t ld, sc_rows_b;
+  float* kl;              // [B, qrows_b]
+};
+hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st);
 
 // Locality counters of rows of selected token indices ([rows, k], k <= 2048).
 hipError_t launch_gather_stats(const int32_t* idx, int32_t* stats, int64_t rows, int k, int page_size,

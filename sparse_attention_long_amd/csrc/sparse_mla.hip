@@ -194,16 +194,14 @@ struct RowState {
   float l_sum;   // this half's share of the softmax denominator
 };
 
-// One chunk of 32 gathered rows: S^T = C.Q^T, softmax weights against the
-// fixed reference, O^T += V^T.P^T.  `valid` bit r says row r of the chunk
-// holds a selected entry.
+// S^T = C.Q^T of one chunk (32 gathered rows x this wave's 32 heads): lane
+// (half, col) gets head col at rows 8*(j/4) + 4*half + j%4, j = 0..15.
 template <int DK, int DV, int NW>
-__device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid, const v8bf (&qb)[DK / 16],
-                                             float zscale, RowState<DK, DV, NW>& rs) {
+__device__ __forceinline__ v16f qk_chunk(const uint16_t* tb, const v8bf (&qb)[DK / 16]) {
   using C = Cfg<DK, DV, NW>;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
-  // ---- S^T = C . Q^T, A operands prefetched kLookA steps ahead
+  // ---- A operands prefetched kLookA steps ahead
   // Lane (row col, half) reads logical piece 2*ks + half of its row.  The
   // swizzle only flips the low two bits of the piece index, so every part-A
   // address is one of two per-lane bases plus a compile-time offset.
@@ -233,6 +231,19 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid,
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(st) : "v"(cur), "v"(qb[ks]));
   }
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(st));
+  return st;
+}
+
+// One chunk of 32 gathered rows: S^T = C.Q^T, softmax weights against the
+// fixed reference, O^T += V^T.P^T.  `valid` bit r says row r of the chunk
+// holds a selected entry.
+template <int DK, int DV, int NW>
+__device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid, const v8bf (&qb)[DK / 16],
+                                             float zscale, RowState<DK, DV, NW>& rs) {
+  using C = Cfg<DK, DV, NW>;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const v16f st = qk_chunk<DK, DV, NW>(tb, qb);
   // ---- mask (only a row's last chunk can hold padding), chunk max
   float z[16];
 #pragma unroll
@@ -454,6 +465,228 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   }
 }
 
+// Forward indexer KL on the selected set (page "6.2 DSA Continued
+// Pre-Training: Warm-up and Sparse Stages", sparse stage; the analysis page,
+// Sec. 1.1 Eq. (4)).  For query row t with selection S:
+//   P_s  = sum_h exp(z_hs - lse_h)     (attention weights of all heads, z_hs =
+//                                       sm_scale q_h . c_s, lse_h the attention's)
+//   p_s  = P_s / T, T = sum_s P_s      (L1 normalisation along the sequence)
+//   ln q_s = I_s - LSE_I,  LSE_I = log sum_{s in S} exp(I_s)
+//   KL   = sum_s p_s (ln p_s - ln q_s) = A / T - ln T,
+//          A = sum_s P_s (ln P_s - I_s + LSE_I).
+// One workgroup per row: the selected rows are gathered through the same
+// three-tile DMA ring as the attention.  The logits are computed as
+// S = Q.C^T (the attention's operands swapped, heads on M, keys on N), so
+// lane (half, col) holds 16 heads of key col and the head sum is lane-local
+// plus one half swap.  The four waves' sums meet in a two-chunk LDS ring
+// that each wave folds (8 keys each) one chunk later; the tile barrier
+// orders the accesses.
+template <int DK, int DV, int NW>
+__device__ __forceinline__ v16f qk_chunk_heads(const uint16_t* tb, const v8bf (&qb)[DK / 16]) {
+  using C = Cfg<DK, DV, NW>;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, col = lane & 31;
+  const int sw = swz_a(col);
+  const uint16_t* a_even = tb + (col * C::kRA + (half ^ sw)) * 8;
+  const uint16_t* a_odd = tb + (col * C::kRA + ((2 + half) ^ sw)) * 8;
+  auto load_b = [&](int ks) {
+    if (2 * ks < C::kPA) return *(const v8bf*)((ks & 1 ? a_odd : a_even) + 32 * (ks >> 1));
+    return *(const v8bf*)(tb + piece_pos<DK, DV, NW>(col, 2 * ks + half));
+  };
+  v16f st;
+  v8bf bbuf[kLookA];
+#pragma unroll
+  for (int j = 0; j < kLookA; ++j) bbuf[j] = load_b(j);
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) {
+    const v8bf cur = bbuf[ks % kLookA];
+    if (ks + kLookA < C::kKS) bbuf[ks % kLookA] = load_b(ks + kLookA);
+    if (ks == 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(qb[ks]), "v"(cur));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(st) : "v"(qb[ks]), "v"(cur));
+  }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(st));
+  return st;
+}
+
+template <int DK, int DV, int NW, bool kPaged>
+__global__ void __launch_bounds__(NW * kWave, 1) indexer_kl_kernel(KlArgs ka) {
+  using C = Cfg<DK, DV, NW>;
+  const AttnArgs& a = ka.at;
+  __shared__ __attribute__((aligned(16))) uint16_t tile0[C::kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t tile1[C::kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t tile2[C::kTileElems];
+  __shared__ int32_t sidx[kMaxSlots];
+  __shared__ float isc[kMaxSlots];
+  __shared__ float ksum[2][NW][kChunk];
+  __shared__ float red[2][NW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int rowid = blockIdx.x;
+  const int b = rowid / a.rows;
+  const int i = rowid % a.rows;
+  const int64_t qrow = (int64_t)b * a.qrows_b + i;
+  const int nchunks = (a.k + kChunk - 1) / kChunk;
+
+  // slots: cache rows (or -1) and the index scores of their tokens
+  const int slen = seq_len_of(a.pk, b, a.S);
+  const float* srow = ka.scores + ((int64_t)b * ka.sc_rows_b + i) * ka.ld;
+  for (int j = threadIdx.x; j < nchunks * kChunk; j += C::kThreads) {
+    int v = -1;
+    float iv = -INFINITY;
+    if (j < a.k) {
+      const int t = a.idx[((int64_t)b * a.idx_rows_b + i) * a.k + j];
+      if (t >= 0 && t < slen) {
+        iv = srow[t];
+        v = kPaged ? (int)cache_row(a.pk, b, a.S, t) : t;
+      }
+    }
+    sidx[j] = v;
+    isc[j] = iv;
+  }
+  __syncthreads();
+  // LSE_I over the selected set: block max, then block sum (fixed orders)
+  float mI = -INFINITY;
+  for (int j = threadIdx.x; j < nchunks * kChunk; j += C::kThreads) mI = fmaxf(mI, isc[j]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mI = fmaxf(mI, __shfl_xor(mI, d, kWave));
+  if (lane == 0) red[0][wave] = mI;
+  __syncthreads();
+  mI = red[0][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mI = fmaxf(mI, red[0][w]);
+  float sI = 0.f;
+  if (mI > -INFINITY)
+    for (int j = threadIdx.x; j < nchunks * kChunk; j += C::kThreads)
+      if (isc[j] > -INFINITY) sI += __expf(isc[j] - mI);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sI += __shfl_xor(sI, d, kWave);
+  if (lane == 0) red[1][wave] = sI;
+  __syncthreads();
+  sI = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) sI += red[1][w];
+  const float lse_i = mI + __logf(sI);
+  if (!(mI > -INFINITY)) {   // empty selection (block-uniform)
+    if (threadIdx.x == 0) ka.kl[qrow] = 0.f;
+    return;
+  }
+
+  // Q of this wave's 32 heads (A operand: lane holds head 32*wave + col), and
+  // the log-sum-exp (log2 units) of the 16 heads of this lane's result rows
+  // 32*wave + 8*(j/4) + 4*half + j%4; heads past H weigh 0.
+  const int h = wave * 32 + col;
+  v8bf qb[C::kKS];
+  {
+    const uint16_t* qp = a.q + (qrow * a.H + min(h, a.H - 1)) * DK + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ++ks) {
+      v8bf v = *(const v8bf*)(qp + 16 * ks);
+      if (h >= a.H) v = (v8bf){};
+      qb[ks] = v;
+    }
+  }
+  float lse2[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int hj = wave * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+    lse2[j] = hj < a.H ? a.lse[qrow * a.H + hj] * kLog2e : INFINITY;   // +inf: weight 0
+  }
+  const float zscale = a.sm_scale * kLog2e;
+  wait_vm<0>();
+  __syncthreads();
+
+  const uint16_t* kvb = kPaged ? a.kv : a.kv + (int64_t)b * a.S * DK;
+  constexpr int ndma = C::kDma / NW;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto gather = [&](uint16_t* fill, int ra, int rb) {
+    if constexpr (C::kRowDma) {
+      RowGather<DK, DV, NW, kPaged> g;
+      g.init(ra, rb, wv);
+      g.issue_all(fill, kvb, wv);
+    } else {
+      ChunkGather<DK, DV, NW> g;
+      g.init(fill, kvb, ra);
+      g.issue_all();
+    }
+  };
+  auto rb_of = [&](int c) {
+    if constexpr (C::kRowDma) return sidx[c * kChunk + RowGather<DK, DV, NW, kPaged>::row_b(wv, lane)];
+    else return 0;
+  };
+  // Each wave folds kChunk / NW keys of a chunk (lanes below that count).
+  constexpr int kFold = kChunk / NW;
+  float acc_a = 0.f, acc_t = 0.f;   // this lane's share of A and T
+  auto fold = [&](int c) {
+    if (lane < kFold) {
+      const int r = wave * kFold + lane;
+      float ps = ksum[c & 1][0][r];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) ps += ksum[c & 1][w][r];
+      const int slot = c * kChunk + r;
+      if (sidx[slot] >= 0 && ps > 0.f) {
+        acc_a += ps * (__logf(ps) - isc[slot] + lse_i);
+        acc_t += ps;
+      }
+    }
+  };
+  auto step = [&](int c, const uint16_t* cur, uint16_t* fill) {
+    const int cn = min(c + 2, nchunks - 1);
+    const int rv = sidx[c * kChunk + (lane & 31)];
+    const int ra = sidx[cn * kChunk + (lane & 31)];
+    const int rb = rb_of(cn);
+    if (c + 1 < nchunks) wait_vm<ndma>(); else wait_vm<0>();
+    // the LDS head sums of chunk c-1 must have landed before wave 0 reads them
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 2 < nchunks) gather(fill, ra, rb);
+    if (c > 0) fold(c - 1);
+    const bool kval = rv >= 0;   // this lane's key (col) is a selected entry
+    const v16f st = qk_chunk_heads<DK, DV, NW>(cur, qb);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ps += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j], zscale, -lse2[j]));
+    ps = sum_halves(ps);   // the wave's 32 heads
+    if (lane < kChunk) ksum[c & 1][wave][lane] = kval ? ps : 0.f;
+  };
+
+  if (nchunks > 0) gather(tile0, sidx[lane & 31], rb_of(0));
+  if (nchunks > 1) gather(tile1, sidx[kChunk + (lane & 31)], rb_of(1));
+  for (int c = 0; c < nchunks; c += 3) {
+    step(c, tile0, tile2);
+    if (c + 1 >= nchunks) break;
+    step(c + 1, tile1, tile0);
+    if (c + 2 >= nchunks) break;
+    step(c + 2, tile2, tile1);
+  }
+  wait_dma();
+  __syncthreads();
+  fold(nchunks - 1);
+  // lanes past kFold hold zeros; fixed butterflies and a fixed wave order
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    acc_a += __shfl_xor(acc_a, d, kWave);
+    acc_t += __shfl_xor(acc_t, d, kWave);
+  }
+  if (lane == 0) {
+    red[0][wave] = acc_a;
+    red[1][wave] = acc_t;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float ta = red[0][0], tt = red[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      ta += red[0][w];
+      tt += red[1][w];
+    }
+    ka.kl[qrow] = tt > 0.f ? ta / tt - __logf(tt) : 0.f;
+  }
+}
+
 // Merge split partials: lse = log sum_j exp(lse_j), o = sum_j exp(lse_j - lse) o_j.
 template <int DV>
 __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
@@ -507,10 +740,27 @@ bool attn_dims_supported(int H, int Dk, int Dv) {
   return false;
 }
 
+template <int DK, int DV, int NW>
+hipError_t launch_kl_cfg(const KlArgs& ka, hipStream_t st) {
+  const unsigned grid = (unsigned)(ka.at.B * ka.at.rows);
+  if (ka.at.pk.page_table)
+    hipLaunchKernelGGL((indexer_kl_kernel<DK, DV, NW, true>), dim3(grid), dim3(NW * kWave), 0, st, ka);
+  else
+    hipLaunchKernelGGL((indexer_kl_kernel<DK, DV, NW, false>), dim3(grid), dim3(NW * kWave), 0, st, ka);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st) {
   if (a.rows <= 0 || a.B <= 0) return hipSuccess;
   if (a.Dk == 576 && a.Dv == 512) return launch_cfg<576, 512, 4>(a, st);
   if (a.Dk == 80 && a.Dv == 64) return launch_cfg<80, 64, 1>(a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_kl(const KlArgs& ka, hipStream_t st) {
+  if (ka.at.rows <= 0 || ka.at.B <= 0) return hipSuccess;
+  if (ka.at.Dk == 576 && ka.at.Dv == 512) return launch_kl_cfg<576, 512, 4>(ka, st);
+  if (ka.at.Dk == 80 && ka.at.Dv == 64) return launch_kl_cfg<80, 64, 1>(ka, st);
   return hipErrorInvalidValue;
 }
 

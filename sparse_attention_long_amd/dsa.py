@@ -21,7 +21,8 @@ EXPORTS = (
     "dsa_indexer_scores", "dsa_topk", "dsa_attn_workspace_size", "dsa_sparse_mla_attn",
     "dsa_forward_workspace_size", "dsa_forward", "dsa_quantize_e4m3", "dsa_cache_append",
     "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged", "dsa_forward_paged",
-    "dsa_gather_stats", "dsa_status_string", "dsa_last_error", "dsa_version",
+    "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_status_string", "dsa_last_error",
+    "dsa_version",
 )
 
 
@@ -82,12 +83,15 @@ def lib():
         L.dsa_forward_paged.argtypes = [D, K, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]
         L.dsa_gather_stats.argtypes = [D, ctypes.c_int32, _P, _P, _P]
+        L.dsa_indexer_kl.argtypes = [D, K, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P]
+        L.dsa_forward_kl.argtypes = [D, K, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.restype = ctypes.c_char_p
         for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_quantize_e4m3",
                   "dsa_cache_append", "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged",
-                  "dsa_forward_paged", "dsa_gather_stats", "dsa_version"):
+                  "dsa_forward_paged", "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -198,3 +202,19 @@ def dsa_forward_paged(dims: Dims, layout: PagedKV, q_idx, q_scale, w_idx, k_idx,
 
 def dsa_gather_stats(dims: Dims, page_size: int, idx, stats, stream=None):
     _check(lib().dsa_gather_stats(ctypes.byref(dims), int(page_size), _ptr(idx), _ptr(stats), _stream(stream)))
+
+
+def dsa_indexer_kl(dims: Dims, layout, q, kv, idx, lse, scores, ld: int, sm_scale: float, kl, stream=None):
+    """layout: a PagedKV, or None for dense caches."""
+    _check(lib().dsa_indexer_kl(ctypes.byref(dims), ctypes.byref(layout) if layout is not None else None, _ptr(q),
+                                _ptr(kv), _ptr(idx), _ptr(lse), _ptr(scores), int(ld), float(sm_scale), _ptr(kl),
+                                _stream(stream)))
+
+
+def dsa_forward_kl(dims: Dims, layout, q_idx, q_scale, w_idx, k_idx, k_scale, q, kv, sm_scale: float, out, lse,
+                   idx_out, kl, ws=None, ws_bytes: int = 0, stream=None):
+    """layout: a PagedKV, or None for dense caches."""
+    _check(lib().dsa_forward_kl(ctypes.byref(dims), ctypes.byref(layout) if layout is not None else None,
+                                _ptr(q_idx), _ptr(q_scale), _ptr(w_idx), _ptr(k_idx), _ptr(k_scale), _ptr(q),
+                                _ptr(kv), float(sm_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(kl), _ptr(ws),
+                                int(ws_bytes), _stream(stream)))

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert dsa.dsa_version() == 102
+    assert dsa.dsa_version() == 103
     L = dsa.lib()
     assert L.dsa_status_string(0) == b"ok"
     assert L.dsa_status_string(3) == b"workspace too small"
@@ -188,3 +188,21 @@ def test_gather_stats_validation():
         with pytest.raises(dsa.DSAError) as e:
             dsa.dsa.dsa_gather_stats(_dims(**kw), ps, FAKE, FAKE, stream=0)
         assert e.value.status == status
+
+
+def test_indexer_kl_validation():
+    d = _dims(batch=2, n_q=1, n_kv=200, topk=16)
+    for kw, status in ((dict(lse=None), dsa.dsa.ERR_INVALID_ARG), (dict(ld=100), dsa.dsa.ERR_INVALID_ARG),
+                       (dict(kl=FAKE + 2), dsa.dsa.ERR_INVALID_ARG), (dict(sm=0.0), dsa.dsa.ERR_INVALID_ARG)):
+        a = dict(lse=FAKE, ld=200, kl=FAKE, sm=0.1)
+        a.update(kw)
+        with pytest.raises(dsa.DSAError) as e:
+            dsa.dsa.dsa_indexer_kl(d, None, FAKE, FAKE, FAKE, a["lse"], FAKE, a["ld"], a["sm"], a["kl"], stream=0)
+        assert e.value.status == status
+    with pytest.raises(dsa.DSAError) as e:   # a paged layout is checked as in the _paged calls
+        dsa.dsa.dsa_indexer_kl(d, _layout(page_size=32), FAKE, FAKE, FAKE, FAKE, FAKE, 200, 0.1, FAKE, stream=0)
+    assert e.value.status == dsa.dsa.ERR_UNSUPPORTED
+    with pytest.raises(dsa.DSAError) as e:   # the training forward needs kl and lse
+        dsa.dsa.dsa_forward_kl(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, FAKE,
+                               ws=FAKE, ws_bytes=1 << 30, stream=0)
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG

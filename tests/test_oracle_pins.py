@@ -391,3 +391,44 @@ def test_varlen_rows_are_the_sequence_tail():
     for L, n_q in ((5, 5), (130, 4)):
         pos = O.varlen_positions(L, n_q)
         assert [O.n_candidates(p, L) for p in pos] == list(range(L - n_q + 1, L + 1))
+
+
+# ------------------------------------------------------------------ indexer KL (Eq. (4))
+def test_indexer_kl_is_zero_when_the_indexer_matches_the_attention():
+    # One head: p is that head's softmax over the set.  Index scores equal to
+    # the head's logits (up to a constant) give softmax(I) = p, so KL = 0;
+    # any other scores give KL > 0 (Gibbs' inequality).
+    rs = np.random.RandomState(51)
+    S, Dk, Dv, sc = 40, 12, 8, 0.3
+    q = rs.randn(1, Dk)
+    kv = rs.randn(S, Dk)
+    sel = np.array([1, 4, 9, 17, 30, 33, -1, -1])
+    logits = sc * (kv @ q[0])
+    assert abs(O.indexer_kl_row(q, kv, sel, logits + 7.5, sc, Dv)) < 1e-12
+    other = logits + rs.randn(S) * 0.5
+    assert O.indexer_kl_row(q, kv, sel, other, sc, Dv) > 1e-4
+
+
+def test_indexer_kl_closed_form_two_entries():
+    # Two selected tokens, H heads with logit gaps d_h: p_1 = mean_h sigmoid(d_h)
+    # (head weights summed then L1-normalised), q_1 = sigmoid(I_1 - I_0);
+    # KL = p0 ln(p0/q0) + p1 ln(p1/q1).
+    rs = np.random.RandomState(52)
+    H, Dk, sc = 3, 6, 0.7
+    q = rs.randn(H, Dk)
+    kv = rs.randn(2, Dk)
+    d = sc * (q @ (kv[1] - kv[0]))
+    p1 = np.mean(1.0 / (1.0 + np.exp(-d)))
+    I = np.array([0.2, -1.1])
+    q1 = 1.0 / (1.0 + np.exp(-(I[1] - I[0])))
+    want = (1 - p1) * np.log((1 - p1) / (1 - q1)) + p1 * np.log(p1 / q1)
+    assert abs(O.indexer_kl_row(q, kv, np.array([0, 1]), I, sc, 4) - want) < 1e-12
+
+
+def test_indexer_kl_ignores_padding_and_order_and_empty_rows():
+    rs = np.random.RandomState(53)
+    q, kv, I = rs.randn(4, 10), rs.randn(30, 10), rs.randn(30)
+    a = O.indexer_kl_row(q, kv, np.array([3, 7, 12, 20, -1]), I, 0.4, 6)
+    b = O.indexer_kl_row(q, kv, np.array([20, -1, 12, 3, 7]), I, 0.4, 6)
+    assert abs(a - b) < 1e-12 and a > 0
+    assert O.indexer_kl_row(q, kv, np.array([-1, -1]), I, 0.4, 6) == 0.0
