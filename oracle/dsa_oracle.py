@@ -275,3 +275,66 @@ def indexer_kl_row(q_t, kv, sel, scores, sm_scale: float, dim_v: int):
     log_q = i_sel - (i_max + np.log(np.exp(i_sel - i_max).sum()))
     nz = p > 0
     return float((p[nz] * (np.log(p[nz]) - log_q[nz])).sum())
+
+
+# ----------------------------------------------------------------- masked MHA mode (short prefill)
+# The analysis page, the MQA-mode discussion with Fig. 7: MLA has two
+# algebraically equal forms.  MHA mode decompresses each latent row into
+# per-head keys and values; MQA mode folds the decompression matrices into
+# the query so that every head reads the shared latent row.  The technical
+# report's Inference Costs paragraph (forum translation, Sec. 3) and the
+# analysis page's Fig. 3 discussion: short prefills use a masked MHA mode
+# that simulates DSA, i.e. dense causal attention in MHA mode in which the
+# keys outside the row's top-k set are masked out.
+#
+# Readings (the pages give no per-head sizes for MHA mode): a latent row is
+# [compressed part (dim_v dims) | rope part (Dk - dim_v dims)]; head h has
+# keys [W_UK[h] c | rope] and values W_UV[h] c, where c is the compressed
+# part and the rope part is shared by all heads; the MHA query of head h is
+# [q_nope (dn dims) | q_rope (Dk - dim_v dims)].
+def mha_decompress(kv, w_uk, w_uv, dim_v: int):
+    """MHA-mode keys and values of latent rows kv [n, Dk].
+    w_uk [H, dn, dim_v], w_uv [H, dvh, dim_v].  Returns k_nope [H, n, dn]
+    with k_nope[h, s] = W_UK[h] c_s, v [H, n, dvh] with v[h, s] = W_UV[h] c_s,
+    and rope [n, Dk - dim_v] (float64)."""
+    c = np.asarray(kv, dtype=np.float64)
+    comp = c[:, :dim_v]
+    k_nope = np.einsum("hdc,sc->hsd", np.asarray(w_uk, dtype=np.float64), comp)
+    v = np.einsum("hdc,sc->hsd", np.asarray(w_uv, dtype=np.float64), comp)
+    return k_nope, v, c[:, dim_v:]
+
+
+def selection_mask(sel, n_keys: int) -> np.ndarray:
+    """Boolean [n_keys]: True at the selected token indices (entries < 0 or
+    >= n_keys are ignored)."""
+    m = np.zeros(n_keys, dtype=bool)
+    s = np.asarray(sel, dtype=np.int64)
+    m[s[(s >= 0) & (s < n_keys)]] = True
+    return m
+
+
+def masked_mha_row(q_t, kv, w_uk, w_uv, sel, p: int, sm_scale: float, dim_v: int):
+    """Masked MHA-mode attention of one query row at absolute position p.
+
+    q_t [H, dn + dr] (decompressed-key dims first, then the rope dims);
+    kv [S, Dk] latent rows.  Every key s <= p (s < S) is scored, keys outside
+    the selection get -inf, and the softmax runs over the row:
+        z[h, s] = sm_scale * (q_nope[h] . W_UK[h] c_s + q_rope[h] . rope_s)
+        out[h]  = sum_s softmax(z[h])_s W_UV[h] c_s
+    Returns out [H, dvh] and lse [H] (float64); a row with no selected key
+    gets out = 0 and lse = -inf."""
+    q = np.asarray(q_t, dtype=np.float64)
+    H, dn = q.shape[0], np.asarray(w_uk).shape[1]
+    n = min(p + 1, np.asarray(kv).shape[0])
+    k_nope, v, rope = mha_decompress(np.asarray(kv)[:n], w_uk, w_uv, dim_v)
+    keep = selection_mask(sel, n)
+    dvh = v.shape[2]
+    if not keep.any():
+        return np.zeros((H, dvh)), np.full(H, -np.inf)
+    z = sm_scale * (np.einsum("hd,hsd->hs", q[:, :dn], k_nope) + q[:, dn:] @ rope.T)   # [H, n]
+    z = np.where(keep[None, :], z, -np.inf)
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    den = e.sum(axis=1, keepdims=True)
+    out = np.einsum("hs,hsd->hd", e / den, v)
+    return out, (zmax + np.log(den))[:, 0]

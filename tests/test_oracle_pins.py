@@ -432,3 +432,84 @@ def test_indexer_kl_ignores_padding_and_order_and_empty_rows():
     b = O.indexer_kl_row(q, kv, np.array([20, -1, 12, 3, 7]), I, 0.4, 6)
     assert abs(a - b) < 1e-12 and a > 0
     assert O.indexer_kl_row(q, kv, np.array([-1, -1]), I, 0.4, 6) == 0.0
+
+
+# ----------------------------------------------------------------- masked MHA mode
+def _mha_case(rs, H=3, dn=5, dr=3, dim_v=7, dvh=4, S=20):
+    kv = rs.randn(S, dim_v + dr)
+    return kv, rs.randn(H, dn, dim_v), rs.randn(H, dvh, dim_v), rs.randn(H, dn + dr)
+
+
+def test_masked_mha_equals_mqa_attention_with_absorbed_query():
+    # Fig. 7 discussion of the analysis page: MHA mode (decompressed per-head
+    # keys/values) and MQA mode (decompression folded into the query) are the
+    # same attention.  MQA form: q_abs[h] = [W_UK[h]^T q_nope[h] | q_rope[h]]
+    # over the latent rows, then W_UV[h] applied to the latent-space output.
+    # Rectangular dims catch a transposed decompression matrix.
+    rs = np.random.RandomState(40)
+    kv, wuk, wuv, _ = _mha_case(rs)
+    dn = wuk.shape[1]
+    for p, sel in ((15, [1, 4, 7, 9, 15, -1, -1]), (6, [0, 1, 2, 3, 4, 5, 6]), (19, [19]), (3, [2, -1])):
+        q = rs.randn(3, dn + 3)
+        o, lse = O.masked_mha_row(q, kv, wuk, wuv, np.array(sel), p, 0.3, 7)
+        q_abs = np.concatenate([np.einsum("hdc,hd->hc", wuk, q[:, :dn]), q[:, dn:]], axis=1)
+        o_lat, lse_lat = O.sparse_mla_row(q_abs, kv, np.array(sel), 0.3, 7)
+        assert np.allclose(o, np.einsum("hdc,hc->hd", wuv, o_lat), rtol=1e-12, atol=1e-12)
+        assert np.allclose(lse, lse_lat, rtol=1e-13)
+
+
+def test_masked_mha_with_every_key_selected_is_dense_causal_sdpa():
+    # Below the top-k size every causal key is selected, so masked MHA mode is
+    # plain causal multi-head attention on the decompressed keys and values:
+    # checked against torch's SDPA in float64.
+    rs = np.random.RandomState(41)
+    L, H, dn, dr, dim_v, dvh = 18, 4, 6, 2, 10, 5
+    kv, wuk, wuv, _ = _mha_case(rs, H, dn, dr, dim_v, dvh, L)
+    q = rs.randn(L, H, dn + dr)
+    got = np.stack([O.masked_mha_row(q[t], kv, wuk, wuv, np.arange(t + 1), t, 0.4, dim_v)[0] for t in range(L)])
+    k = np.concatenate([np.einsum("hdc,sc->hsd", wuk, kv[:, :dim_v]),
+                        np.broadcast_to(kv[None, :, dim_v:], (H, L, dr))], axis=2)
+    v = np.einsum("hdc,sc->hsd", wuv, kv[:, :dim_v])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2).contiguous(), torch.from_numpy(k.copy()), torch.from_numpy(v),
+        is_causal=True, scale=0.4)
+    assert np.allclose(got, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_masked_mha_mask_is_a_boolean_sdpa_mask_and_drops_future_keys():
+    # The selection acts as a boolean attention mask over the causal keys;
+    # entries past the row's position or padding change nothing.
+    rs = np.random.RandomState(42)
+    L, H, dn, dr, dim_v, dvh = 16, 2, 4, 4, 8, 4
+    kv, wuk, wuv, _ = _mha_case(rs, H, dn, dr, dim_v, dvh, L)
+    q = rs.randn(L, H, dn + dr)
+    allowed = np.zeros((L, L), dtype=bool)
+    got = []
+    for t in range(L):
+        sel = np.sort(rs.choice(t + 1, size=min(t + 1, 5), replace=False))
+        allowed[t, sel] = True
+        noisy = np.concatenate([sel, [t + 1 + j for j in range(2) if t + 1 + j < L], [-1, -1]])
+        got.append(O.masked_mha_row(q[t], kv, wuk, wuv, noisy, t, 0.5, dim_v))
+    k = np.concatenate([np.einsum("hdc,sc->hsd", wuk, kv[:, :dim_v]),
+                        np.broadcast_to(kv[None, :, dim_v:], (H, L, dr))], axis=2)
+    v = np.einsum("hdc,sc->hsd", wuv, kv[:, :dim_v])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2).contiguous(), torch.from_numpy(k.copy()), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(allowed), scale=0.5)
+    assert np.allclose(np.stack([g[0] for g in got]), ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_masked_mha_single_key_and_empty_rows():
+    rs = np.random.RandomState(43)
+    kv, wuk, wuv, q = _mha_case(rs)
+    o, lse = O.masked_mha_row(q, kv, wuk, wuv, np.array([6, -1]), 9, 0.3, 7)
+    assert np.allclose(o, wuv @ kv[6, :7], rtol=1e-13)
+    z = 0.3 * (np.einsum("hd,hd->h", q[:, :5], wuk @ kv[6, :7]) + q[:, 5:] @ kv[6, 7:])
+    assert np.allclose(lse, z, rtol=1e-13)
+    o, lse = O.masked_mha_row(q, kv, wuk, wuv, np.array([12, -1]), 9, 0.3, 7)   # only a future key
+    assert np.array_equal(o, np.zeros_like(o)) and np.all(lse == -np.inf)
+
+
+def test_selection_mask_bits():
+    m = O.selection_mask(np.array([0, 3, 3, 31, 32, -1, 40, 7]), 33)
+    assert np.flatnonzero(m).tolist() == [0, 3, 7, 31, 32]
