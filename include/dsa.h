@@ -269,6 +269,67 @@ int dsa_forward_kl(const dsa_dims* dims, const dsa_paged_kv* layout, const uint8
                    const uint16_t* kv, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, float* kl,
                    void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Masked MHA mode for short prefills (the technical report's Inference Costs
+ * paragraph, forum translation Sec. 3: short prefills simulate DSA with a
+ * masked MHA mode; the analysis page's Fig. 3 discussion; MHA and MQA as the
+ * two equal forms of MLA, the analysis page around Fig. 7).
+ *
+ * MHA mode splits a latent row c_s (dim_qk dims) into its compressed part
+ * c_s[0:dim_v] and its rope part c_s[dim_v:dim_qk] (shared by the heads).
+ * Head h has the decompression matrices W_UK[h] [dim_nope, dim_v] and
+ * W_UV[h] [dim_vh, dim_v]; its key of token s is
+ * [W_UK[h] c_s[0:dim_v] | c_s[dim_v:]] and its value W_UV[h] c_s[0:dim_v].
+ * The MHA query of head h is q_mha[b, i, h] = [q_nope (dim_nope) | q_rope
+ * (dim_qk - dim_v)].  Masked MHA attention of row i (position p):
+ *   z_s   = sm_scale * q_mha[b,i,h] . key_h(s)    over s <= p with mask bit set
+ *   out   = sum_s softmax(z)_s value_h(s),   lse = log sum_s exp(z_s)
+ * With the mask taken from the row's top-k selection this equals, up to
+ * rounding, W_UV[h] applied to dsa_sparse_mla_attn's output for the absorbed
+ * query [W_UK[h]^T q_nope | q_rope].
+ *
+ * Supported: (dim_nope, rope = dim_qk - dim_v, dim_vh) = (128, 64, 128) or
+ * (32, 16, 32); dim_v a multiple of 64; heads <= 128; n_kv <= 65536.
+ */
+
+/* Selection bitmap: mask [B, ceil(n_kv / 32), n_q] uint32; bit r of word
+ * (b, c, i) is set iff token 32c + r is in row i's list idx[b, i, 0:topk]
+ * and visible to the row (32c + r <= p, < n_kv).  Every word is written. */
+int dsa_selection_mask(const dsa_dims* dims, const int32_t* idx, uint32_t* mask, void* stream);
+
+/* Per-head keys and values of latent rows s < n_rows (0 <= n_rows <= n_kv):
+ *   k_mha [B, H, n_kv, dim_nope] bf16:  k_mha[b,h,s] = W_UK[h] kv[b,s,0:dim_v]
+ *   v_mha [B, H, n_kv, dim_vh]   bf16:  v_mha[b,h,s] = W_UV[h] kv[b,s,0:dim_v]
+ * w_uk [H, dim_nope, dim_v], w_uv [H, dim_vh, dim_v] bf16.  bf16 MFMA with
+ * fp32 accumulation, rounded once to bf16.  Rows >= n_rows are not written. */
+int dsa_mha_decompress(const dsa_dims* dims, int32_t dim_nope, int32_t dim_vh, const uint16_t* kv, const uint16_t* w_uk,
+                       const uint16_t* w_uv, int32_t n_rows, uint16_t* k_mha, uint16_t* v_mha, void* stream);
+
+/* Masked MHA attention.  q_mha [B, T, H, dim_nope + dim_qk - dim_v] bf16,
+ * kv [B, S, dim_qk] (rope dims read), k_mha / v_mha as written by
+ * dsa_mha_decompress (rows s < q_pos0 + n_q must hold finite values),
+ * mask as written by dsa_selection_mask (any bit pattern is allowed: the
+ * causal limit is applied as well).  out [B, T, H, dim_vh] bf16, lse
+ * [B, T, H] f32 or NULL; a row with no visible selected key gets out = 0
+ * and lse = -inf.  bf16 MFMA, fp32 accumulation and softmax. */
+int dsa_masked_mha_attn(const dsa_dims* dims, int32_t dim_nope, int32_t dim_vh, const uint16_t* q_mha,
+                        const uint16_t* kv, const uint16_t* k_mha, const uint16_t* v_mha, const uint32_t* mask,
+                        float sm_scale, uint16_t* out, float* lse, void* stream);
+
+/* Whole short-prefill path: indexer -> top-k -> selection mask (in chunks
+ * of query rows, as dsa_forward) -> decompression of the rows s < q_pos0 +
+ * n_q -> masked MHA attention.  Inputs as in dsa_forward plus q_mha, w_uk
+ * and w_uv; idx_out [B, T, topk] or NULL receives the selection.  Equal, bit
+ * for bit, to running the five calls one after the other.  ws must hold
+ * dsa_masked_mha_workspace_size(dims, dim_nope, dim_vh) bytes (256-byte
+ * aligned). */
+size_t dsa_masked_mha_workspace_size(const dsa_dims* dims, int32_t dim_nope, int32_t dim_vh);
+int dsa_masked_mha_forward(const dsa_dims* dims, int32_t dim_nope, int32_t dim_vh, const uint8_t* q_idx,
+                           const float* q_scale, const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale,
+                           const uint16_t* q_mha, const uint16_t* kv, const uint16_t* w_uk, const uint16_t* w_uv,
+                           float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* Status text, thread-local last error message, ABI version (major*100+minor). */
 const char* dsa_status_string(int status);
 const char* dsa_last_error(void);

@@ -299,8 +299,8 @@ def mha_decompress(kv, w_uk, w_uv, dim_v: int):
     and rope [n, Dk - dim_v] (float64)."""
     c = np.asarray(kv, dtype=np.float64)
     comp = c[:, :dim_v]
-    k_nope = np.einsum("hdc,sc->hsd", np.asarray(w_uk, dtype=np.float64), comp)
-    v = np.einsum("hdc,sc->hsd", np.asarray(w_uv, dtype=np.float64), comp)
+    k_nope = np.matmul(comp[None], np.asarray(w_uk, dtype=np.float64).transpose(0, 2, 1))
+    v = np.matmul(comp[None], np.asarray(w_uv, dtype=np.float64).transpose(0, 2, 1))
     return k_nope, v, c[:, dim_v:]
 
 
@@ -313,7 +313,7 @@ def selection_mask(sel, n_keys: int) -> np.ndarray:
     return m
 
 
-def masked_mha_row(q_t, kv, w_uk, w_uv, sel, p: int, sm_scale: float, dim_v: int):
+def masked_mha_row(q_t, kv, w_uk, w_uv, sel, p: int, sm_scale: float, dim_v: int, kvh=None):
     """Masked MHA-mode attention of one query row at absolute position p.
 
     q_t [H, dn + dr] (decompressed-key dims first, then the rope dims);
@@ -322,11 +322,14 @@ def masked_mha_row(q_t, kv, w_uk, w_uv, sel, p: int, sm_scale: float, dim_v: int
         z[h, s] = sm_scale * (q_nope[h] . W_UK[h] c_s + q_rope[h] . rope_s)
         out[h]  = sum_s softmax(z[h])_s W_UV[h] c_s
     Returns out [H, dvh] and lse [H] (float64); a row with no selected key
-    gets out = 0 and lse = -inf."""
+    gets out = 0 and lse = -inf.  kvh: mha_decompress(kv[:m], ...) for some
+    m >= min(p + 1, S), to share one decompression between rows."""
     q = np.asarray(q_t, dtype=np.float64)
     H, dn = q.shape[0], np.asarray(w_uk).shape[1]
     n = min(p + 1, np.asarray(kv).shape[0])
-    k_nope, v, rope = mha_decompress(np.asarray(kv)[:n], w_uk, w_uv, dim_v)
+    if kvh is None:
+        kvh = mha_decompress(np.asarray(kv)[:n], w_uk, w_uv, dim_v)
+    k_nope, v, rope = kvh[0][:, :n], kvh[1][:, :n], kvh[2][:n]
     keep = selection_mask(sel, n)
     dvh = v.shape[2]
     if not keep.any():

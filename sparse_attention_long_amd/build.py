@@ -23,7 +23,7 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
-DSA_SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "quant.hip", "paged.hip"]
+DSA_SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "quant.hip", "paged.hip", "masked_mha.hip"]
 LIB_DSA = os.path.join(HERE, "libdsa.so")
 LIB_SYNTH = os.path.join(ROOT, "synth", "libdsa_synth.so")
 

@@ -181,7 +181,7 @@ dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const flo
 
 extern "C" {
 
-int dsa_version(void) { return 103; }
+int dsa_version(void) { return 104; }
 
 const char* dsa_status_string(int status) {
   switch (status) {
@@ -573,6 +573,210 @@ int dsa_cache_append(const dsa_dims* d, const void* k_new, int k_dtype, const ui
   if (st != DSA_OK || !kv) return st;
   return hip_status(dsa::launch_copy_rows(kv_new, kv, n, d->dim_qk, d->n_q, d->n_kv, d->q_pos0, s),
                     "cache append (latents)");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- masked MHA mode (short prefill)
+namespace {
+
+constexpr int kMhaMaxKv = 65536;   // the selection bitmap of a row is staged whole in LDS
+
+int check_mha(const dsa_dims* d, int dn, int dvh) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  REQUIRE(d->heads >= 1 && d->heads <= 128, DSA_ERR_UNSUPPORTED, "heads must be in [1, 128] (got %d)", d->heads);
+  REQUIRE(d->dim_v >= 1 && d->dim_v < d->dim_qk, DSA_ERR_INVALID_ARG,
+          "dim_v (%d) must be below dim_qk (%d): MHA mode needs rope dims", d->dim_v, d->dim_qk);
+  REQUIRE(dsa::mha_dims_supported(dn, d->dim_qk - d->dim_v, dvh, d->dim_v), DSA_ERR_UNSUPPORTED,
+          "MHA dims (dim_nope %d, rope %d, dim_vh %d, dim_v %d) not built; supported: 128/64/128 and 32/16/32 "
+          "with dim_v a multiple of 64",
+          dn, d->dim_qk - d->dim_v, dvh, d->dim_v);
+  REQUIRE(d->n_kv <= kMhaMaxKv, DSA_ERR_UNSUPPORTED, "masked MHA mode supports n_kv <= %d (got %d)", kMhaMaxKv,
+          d->n_kv);
+  return DSA_OK;
+}
+
+int mha_nc(const dsa_dims* d) { return (d->n_kv + 31) / 32; }
+
+int mask_impl(const dsa_dims* d, const int32_t* idx, int64_t idx_rows_b, int rows, int row0, uint32_t* mask,
+              hipStream_t s) {
+  dsa::MaskArgs m{};
+  m.idx = idx;
+  m.mask = mask;
+  m.idx_rows_b = idx_rows_b;
+  m.B = d->batch;
+  m.rows = rows;
+  m.row0 = row0;
+  m.T = d->n_q;
+  m.S = d->n_kv;
+  m.k = d->topk;
+  m.pos0 = d->q_pos0;
+  m.NC = mha_nc(d);
+  return hip_status(dsa::launch_selection_mask(m, s), "selection mask launch");
+}
+
+int decompress_impl(const dsa_dims* d, int dn, int dvh, const uint16_t* kv, const uint16_t* w_uk,
+                    const uint16_t* w_uv, int n_rows, int S_h, uint16_t* k_mha, uint16_t* v_mha, hipStream_t s) {
+  dsa::DecompArgs a{};
+  a.kv = kv;
+  a.w[0] = w_uk;
+  a.w[1] = w_uv;
+  a.out[0] = k_mha;
+  a.out[1] = v_mha;
+  a.rows_w[0] = dn;
+  a.rows_w[1] = dvh;
+  a.B = d->batch;
+  a.S = d->n_kv;
+  a.H = d->heads;
+  a.Dk = d->dim_qk;
+  a.Dv = d->dim_v;
+  a.n_rows = n_rows;
+  a.S_h = S_h;
+  return hip_status(dsa::launch_mha_decompress(a, s), "MHA decompression launch");
+}
+
+int mha_attn_launch(const dsa_dims* d, int dn, int dvh, const uint16_t* q_mha, const uint16_t* kv,
+                    const uint16_t* k_mha, const uint16_t* v_mha, int S_h, const uint32_t* mask, float sm_scale,
+                    uint16_t* out, float* lse, hipStream_t s) {
+  dsa::MhaArgs a{};
+  a.q = q_mha;
+  a.kv = kv;
+  a.kh = k_mha;
+  a.vh = v_mha;
+  a.mask = mask;
+  a.out = out;
+  a.lse = lse;
+  a.B = d->batch;
+  a.T = d->n_q;
+  a.S = d->n_kv;
+  a.S_h = S_h;
+  a.H = d->heads;
+  a.Dk = d->dim_qk;
+  a.Dv = d->dim_v;
+  a.pos0 = d->q_pos0;
+  a.NC = mha_nc(d);
+  a.sm_scale = sm_scale;
+  return hip_status(dsa::launch_masked_mha(a, dn, d->dim_qk - d->dim_v, dvh, s), "masked MHA launch");
+}
+
+struct MhaLayout {
+  int64_t tc;
+  size_t scores_off, idx_off, mask_off, k_off, v_off, total;
+};
+
+MhaLayout mha_layout(const dsa_dims* d, int dn, int dvh) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  MhaLayout L;
+  L.tc = forward_chunk_rows(d);
+  const size_t rows_h = (size_t)d->q_pos0 + d->n_q;   // keys any row can see
+  L.scores_off = 0;
+  L.idx_off = up((size_t)d->batch * L.tc * d->n_kv * sizeof(float));
+  L.mask_off = L.idx_off + up((size_t)d->batch * L.tc * d->topk * sizeof(int32_t));
+  L.k_off = L.mask_off + up((size_t)d->batch * mha_nc(d) * d->n_q * sizeof(uint32_t));
+  L.v_off = L.k_off + up((size_t)d->batch * d->heads * rows_h * dn * 2);
+  L.total = L.v_off + up((size_t)d->batch * d->heads * rows_h * dvh * 2);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_selection_mask(const dsa_dims* d, const int32_t* idx, uint32_t* mask, void* stream) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  REQUIRE(d->n_kv <= kMhaMaxKv, DSA_ERR_UNSUPPORTED, "selection masks support n_kv <= %d (got %d)", kMhaMaxKv,
+          d->n_kv);
+  REQUIRE(idx && mask, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(idx, 4) && aligned(mask, 4), DSA_ERR_INVALID_ARG, "idx and mask must be 4-byte aligned");
+  return mask_impl(d, idx, d->n_q, d->n_q, 0, mask, (hipStream_t)stream);
+}
+
+int dsa_mha_decompress(const dsa_dims* d, int32_t dim_nope, int32_t dim_vh, const uint16_t* kv, const uint16_t* w_uk,
+                       const uint16_t* w_uv, int32_t n_rows, uint16_t* k_mha, uint16_t* v_mha, void* stream) {
+  int st;
+  if ((st = check_mha(d, dim_nope, dim_vh)) != DSA_OK) return st;
+  REQUIRE(kv && w_uk && w_uv && k_mha && v_mha, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(kv, 16) && aligned(w_uk, 16) && aligned(w_uv, 16) && aligned(k_mha, 16) && aligned(v_mha, 16),
+          DSA_ERR_INVALID_ARG, "kv, w_uk, w_uv, k_mha and v_mha must be 16-byte aligned");
+  REQUIRE(n_rows >= 0 && n_rows <= d->n_kv, DSA_ERR_INVALID_ARG, "n_rows (%d) must be in [0, n_kv = %d]", n_rows,
+          d->n_kv);
+  return decompress_impl(d, dim_nope, dim_vh, kv, w_uk, w_uv, n_rows, d->n_kv, k_mha, v_mha, (hipStream_t)stream);
+}
+
+int dsa_masked_mha_attn(const dsa_dims* d, int32_t dim_nope, int32_t dim_vh, const uint16_t* q_mha,
+                        const uint16_t* kv, const uint16_t* k_mha, const uint16_t* v_mha, const uint32_t* mask,
+                        float sm_scale, uint16_t* out, float* lse, void* stream) {
+  int st;
+  if ((st = check_mha(d, dim_nope, dim_vh)) != DSA_OK) return st;
+  REQUIRE(q_mha && kv && k_mha && v_mha && mask && out, DSA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned(q_mha, 16) && aligned(kv, 16) && aligned(k_mha, 16) && aligned(v_mha, 16) && aligned(out, 16) &&
+              aligned(mask, 4) && aligned(lse, 4),
+          DSA_ERR_INVALID_ARG, "q_mha, kv, k_mha, v_mha and out must be 16-byte aligned; mask and lse 4-byte aligned");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  return mha_attn_launch(d, dim_nope, dim_vh, q_mha, kv, k_mha, v_mha, d->n_kv, mask, sm_scale, out, lse,
+                         (hipStream_t)stream);
+}
+
+size_t dsa_masked_mha_workspace_size(const dsa_dims* d, int32_t dim_nope, int32_t dim_vh) {
+  if (check_mha(d, dim_nope, dim_vh) != DSA_OK || check_indexer_dims(d) != DSA_OK) return 0;
+  return mha_layout(d, dim_nope, dim_vh).total;
+}
+
+int dsa_masked_mha_forward(const dsa_dims* d, int32_t dim_nope, int32_t dim_vh, const uint8_t* q_idx,
+                           const float* q_scale, const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale,
+                           const uint16_t* q_mha, const uint16_t* kv, const uint16_t* w_uk, const uint16_t* w_uv,
+                           float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int st;
+  if ((st = check_mha(d, dim_nope, dim_vh)) != DSA_OK) return st;
+  if ((st = check_indexer_dims(d)) != DSA_OK) return st;
+  REQUIRE(q_idx && q_scale && w_idx && k_idx && k_scale && q_mha && kv && w_uk && w_uv && out, DSA_ERR_INVALID_ARG,
+          "null tensor pointer");
+  REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16), DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+  REQUIRE(aligned(q_scale, 4) && aligned(k_scale, 4) && aligned(w_idx, 2) && aligned(idx_out, 4) && aligned(lse, 4),
+          DSA_ERR_INVALID_ARG, "misaligned scale/weight/idx/lse pointer");
+  REQUIRE(aligned(q_mha, 16) && aligned(kv, 16) && aligned(w_uk, 16) && aligned(w_uv, 16) && aligned(out, 16),
+          DSA_ERR_INVALID_ARG, "q_mha, kv, w_uk, w_uv and out must be 16-byte aligned");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const MhaLayout L = mha_layout(d, dim_nope, dim_vh);
+  REQUIRE(ws != nullptr && ws_bytes >= L.total, DSA_ERR_WORKSPACE,
+          "masked MHA forward needs %zu workspace bytes (got %zu)", L.total, ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  const hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  float* sc = (float*)(wsb + L.scores_off);
+  uint32_t* mask = (uint32_t*)(wsb + L.mask_off);
+  uint16_t* k_mha = (uint16_t*)(wsb + L.k_off);
+  uint16_t* v_mha = (uint16_t*)(wsb + L.v_off);
+  const bool decode_form = d->n_q <= dsa::kIndexerDecodeMaxRows;
+  for (int64_t i0 = 0; i0 < d->n_q; i0 += L.tc) {
+    const int rows = (int)((d->n_q - i0) < L.tc ? (d->n_q - i0) : L.tc);
+    const dsa::IndexerArgs ia =
+        indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, sc, d->n_kv, i0, rows, L.tc, dsa::PagedKV{});
+    hipError_t e = dsa::launch_indexer(ia, decode_form, s);
+    if (e != hipSuccess) return hip_status(e, "indexer launch");
+    dsa::TopkArgs ta{};
+    ta.scores = sc;
+    ta.ld = d->n_kv;
+    ta.sc_rows_b = L.tc;
+    ta.idx = idx_out ? idx_out + i0 * d->topk : (int32_t*)(wsb + L.idx_off);
+    ta.idx_rows_b = idx_out ? d->n_q : L.tc;
+    ta.B = d->batch;
+    ta.rows = rows;
+    ta.pos0 = d->q_pos0 + (int)i0;
+    ta.S = d->n_kv;
+    ta.k = d->topk;
+    e = dsa::launch_topk(ta, s);
+    if (e != hipSuccess) return hip_status(e, "top-k launch");
+    if ((st = mask_impl(d, ta.idx, ta.idx_rows_b, rows, (int)i0, mask, s)) != DSA_OK) return st;
+  }
+  const int rows_h = d->q_pos0 + d->n_q;
+  if ((st = decompress_impl(d, dim_nope, dim_vh, kv, w_uk, w_uv, rows_h, rows_h, k_mha, v_mha, s)) != DSA_OK)
+    return st;
+  return mha_attn_launch(d, dim_nope, dim_vh, q_mha, kv, k_mha, v_mha, rows_h, mask, sm_scale, out, lse, s);
 }
 
 }  // extern "C"

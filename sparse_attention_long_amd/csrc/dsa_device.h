@@ -115,6 +115,11 @@ __device__ __forceinline__ void dma_x4_s(uint32_t voff, const void* sbase, uint3
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_base));
 }
+__device__ __forceinline__ void dma_x1_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_base));
+}
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace dsa

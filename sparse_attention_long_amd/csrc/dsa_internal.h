@@ -102,6 +102,42 @@ hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st);
 hipError_t launch_gather_stats(const int32_t* idx, int32_t* stats, int64_t rows, int k, int page_size,
                                hipStream_t st);
 
+// Masked MHA mode (short prefill).
+// Selection bitmap: rows [0, rows) of a span whose row r is query row
+// row0 + r (absolute position pos0 + row0 + r) of each sequence; its index
+// list is idx[(b * idx_rows_b + r) * k ...].  Writes words (b, c, row0 + r)
+// of mask [B, NC, T] for every c < NC.
+struct MaskArgs {
+  const int32_t* idx;
+  uint32_t* mask;
+  int64_t idx_rows_b;
+  int B, rows, row0, T, S, k, pos0, NC;
+};
+// Per-head decompression of latent rows [0, n_rows): out[m][b, h, s, :] =
+// W_m[h] . kv[b, s, 0:Dv] for m = 0 (keys, rows_w[0] dims) and 1 (values).
+struct DecompArgs {
+  const uint16_t* kv;         // [B, S, Dk]
+  const uint16_t* w[2];       // [H, rows_w[m], Dv]
+  uint16_t* out[2];           // [B, H, S_h, rows_w[m]]
+  int rows_w[2];
+  int B, S, H, Dk, Dv, n_rows, S_h;
+};
+struct MhaArgs {
+  const uint16_t* q;          // [B, T, H, dn + dr]
+  const uint16_t* kv;         // [B, S, Dk] (rope dims [Dv, Dk))
+  const uint16_t* kh;         // [B, H, S_h, dn]
+  const uint16_t* vh;         // [B, H, S_h, dvh]
+  const uint32_t* mask;       // [B, NC, T]
+  uint16_t* out;              // [B, T, H, dvh]
+  float* lse;                 // [B, T, H] or null
+  int B, T, S, S_h, H, Dk, Dv, pos0, NC;
+  float sm_scale;
+};
+bool mha_dims_supported(int dn, int dr, int dvh, int Dv);
+hipError_t launch_selection_mask(const MaskArgs& a, hipStream_t st);
+hipError_t launch_mha_decompress(const DecompArgs& a, hipStream_t st);
+hipError_t launch_masked_mha(const MhaArgs& a, int dn, int dr, int dvh, hipStream_t st);
+
 // Shape support checks (true if the kernels are built for these dims).
 bool attn_dims_supported(int H, int Dk, int Dv);
 int topk_max_kv();

@@ -21,8 +21,9 @@ EXPORTS = (
     "dsa_indexer_scores", "dsa_topk", "dsa_attn_workspace_size", "dsa_sparse_mla_attn",
     "dsa_forward_workspace_size", "dsa_forward", "dsa_quantize_e4m3", "dsa_cache_append",
     "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged", "dsa_forward_paged",
-    "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_status_string", "dsa_last_error",
-    "dsa_version",
+    "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_selection_mask", "dsa_mha_decompress",
+    "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size", "dsa_masked_mha_forward", "dsa_status_string",
+    "dsa_last_error", "dsa_version",
 )
 
 
@@ -86,12 +87,21 @@ def lib():
         L.dsa_indexer_kl.argtypes = [D, K, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P]
         L.dsa_forward_kl.argtypes = [D, K, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]
+        I32 = ctypes.c_int32
+        L.dsa_selection_mask.argtypes = [D, _P, _P, _P]
+        L.dsa_mha_decompress.argtypes = [D, I32, I32, _P, _P, _P, I32, _P, _P, _P]
+        L.dsa_masked_mha_attn.argtypes = [D, I32, I32, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+        L.dsa_masked_mha_workspace_size.argtypes = [D, I32, I32]
+        L.dsa_masked_mha_workspace_size.restype = ctypes.c_size_t
+        L.dsa_masked_mha_forward.argtypes = [D, I32, I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                             _P, _P, _P, ctypes.c_size_t, _P]
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.restype = ctypes.c_char_p
         for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_quantize_e4m3",
                   "dsa_cache_append", "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged",
-                  "dsa_forward_paged", "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_version"):
+                  "dsa_forward_paged", "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_selection_mask",
+                  "dsa_mha_decompress", "dsa_masked_mha_attn", "dsa_masked_mha_forward", "dsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -218,3 +228,33 @@ def dsa_forward_kl(dims: Dims, layout, q_idx, q_scale, w_idx, k_idx, k_scale, q,
                                 _ptr(q_idx), _ptr(q_scale), _ptr(w_idx), _ptr(k_idx), _ptr(k_scale), _ptr(q),
                                 _ptr(kv), float(sm_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(kl), _ptr(ws),
                                 int(ws_bytes), _stream(stream)))
+
+
+def dsa_selection_mask(dims: Dims, idx, mask, stream=None):
+    _check(lib().dsa_selection_mask(ctypes.byref(dims), _ptr(idx), _ptr(mask), _stream(stream)))
+
+
+def dsa_mha_decompress(dims: Dims, dim_nope: int, dim_vh: int, kv, w_uk, w_uv, n_rows: int, k_mha, v_mha,
+                       stream=None):
+    _check(lib().dsa_mha_decompress(ctypes.byref(dims), int(dim_nope), int(dim_vh), _ptr(kv), _ptr(w_uk), _ptr(w_uv),
+                                    int(n_rows), _ptr(k_mha), _ptr(v_mha), _stream(stream)))
+
+
+def dsa_masked_mha_attn(dims: Dims, dim_nope: int, dim_vh: int, q_mha, kv, k_mha, v_mha, mask, sm_scale: float, out,
+                        lse=None, stream=None):
+    _check(lib().dsa_masked_mha_attn(ctypes.byref(dims), int(dim_nope), int(dim_vh), _ptr(q_mha), _ptr(kv),
+                                     _ptr(k_mha), _ptr(v_mha), _ptr(mask), float(sm_scale), _ptr(out), _ptr(lse),
+                                     _stream(stream)))
+
+
+def dsa_masked_mha_workspace_size(dims: Dims, dim_nope: int, dim_vh: int) -> int:
+    return int(lib().dsa_masked_mha_workspace_size(ctypes.byref(dims), int(dim_nope), int(dim_vh)))
+
+
+def dsa_masked_mha_forward(dims: Dims, dim_nope: int, dim_vh: int, q_idx, q_scale, w_idx, k_idx, k_scale, q_mha, kv,
+                           w_uk, w_uv, sm_scale: float, out, lse=None, idx_out=None, ws=None, ws_bytes: int = 0,
+                           stream=None):
+    _check(lib().dsa_masked_mha_forward(ctypes.byref(dims), int(dim_nope), int(dim_vh), _ptr(q_idx), _ptr(q_scale),
+                                        _ptr(w_idx), _ptr(k_idx), _ptr(k_scale), _ptr(q_mha), _ptr(kv), _ptr(w_uk),
+                                        _ptr(w_uv), float(sm_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws),
+                                        int(ws_bytes), _stream(stream)))

@@ -79,6 +79,27 @@ def fill_inputs(wl: Workload, device="cuda"):
     return t
 
 
+def fill_mha(wl: Workload, device="cuda"):
+    """MHA-mode inputs of `wl` on the device: q_mha int16 (bf16 bits)
+    [B,T,H,dn+dr], w_uk [H,dn,Dv], w_uv [H,dvh,Dv]."""
+    import torch
+    from .workloads import mha_dims, mha_w_exp2
+    L = lib()
+    B, T, H, Dv = wl.batch, wl.n_q, wl.heads, wl.dim_v
+    dn, dr, dvh = mha_dims(wl)
+    st = _stream(torch)
+    t = {
+        "q_mha": torch.empty((B, T, H, dn + dr), dtype=torch.int16, device=device),
+        "w_uk": torch.empty((H, dn, Dv), dtype=torch.int16, device=device),
+        "w_uv": torch.empty((H, dvh, Dv), dtype=torch.int16, device=device),
+    }
+    _check(L.synth_fill_bf16(wl.seed, gen.TID["q_mha"], 0, t["q_mha"].numel(), 0, t["q_mha"].data_ptr(), st))
+    e = mha_w_exp2(wl)
+    _check(L.synth_fill_bf16(wl.seed, gen.TID["w_uk"], 0, t["w_uk"].numel(), e, t["w_uk"].data_ptr(), st))
+    _check(L.synth_fill_bf16(wl.seed, gen.TID["w_uv"], 0, t["w_uv"].numel(), e, t["w_uv"].data_ptr(), st))
+    return t
+
+
 def fill_paged(wl: Workload, layout, device="cuda"):
     """Inputs of `wl` with the caches moved into page pools per `layout`
     (synth.workloads.PagedLayout): the dict of fill_inputs with k_idx,

@@ -48,6 +48,9 @@ TID = {
     "lr_ak": 8,   # low-rank loading for k_idx
     "lr_ec": 9,   # noise for kv
     "lr_ek": 10,  # noise for k_idx
+    "q_mha": 11,  # MHA-mode per-head queries [q_nope | q_rope]
+    "w_uk": 12,   # MHA-mode key decompression matrices
+    "w_uv": 13,   # MHA-mode value decompression matrices
 }
 
 E4M3_MAX = 448.0

@@ -190,6 +190,41 @@ def host_inputs(wl: Workload):
     }
 
 
+# ----------------------------------------------------------------- MHA mode (masked short prefill)
+def mha_dims(wl: Workload):
+    """(dn, dr, dvh): per-head decompressed key dims, shared rope dims and
+    value dims of MHA mode.  128 / 64 / 128 for 576-d latents with 512
+    compressed dims (a 192-d per-head query, matching the 1/sqrt(192)
+    softmax scale); half the compressed width for the small shapes."""
+    dr = wl.dim_qk - wl.dim_v
+    dn = 128 if wl.dim_v >= 512 else wl.dim_v // 2
+    return dn, dr, dn
+
+
+def mha_w_exp2(wl: Workload) -> int:
+    """Decompression weights are z * 2^e with 2^e close to 1/sqrt(dim_v), so
+    the per-head keys and values have about unit size."""
+    return -int(math.floor(math.log2(wl.dim_v) / 2))
+
+
+def q_mha_bf16(wl: Workload, b: int, rows) -> np.ndarray:
+    """bf16 bits [n, H, dn + dr] of the MHA-mode queries of rows `rows`."""
+    dn, dr, _ = mha_dims(wl)
+    hd = wl.heads * (dn + dr)
+    out = [gen.normal_f32(wl.seed, gen.TID["q_mha"], (b * wl.n_q + int(i)) * hd, hd) for i in rows]
+    raw = np.stack(out) if out else np.zeros((0, hd), np.float32)
+    return gen.f32_to_bf16_bits(raw).reshape(len(out), wl.heads, dn + dr)
+
+
+def w_mha_bf16(wl: Workload, which: str) -> np.ndarray:
+    """bf16 bits of W_UK [H, dn, dim_v] ("w_uk") or W_UV [H, dvh, dim_v] ("w_uv")."""
+    dn, _, dvh = mha_dims(wl)
+    rows = dn if which == "w_uk" else dvh
+    n = wl.heads * rows * wl.dim_v
+    raw = gen.normal_f32(wl.seed, gen.TID[which], 0, n) * np.float32(2.0 ** mha_w_exp2(wl))
+    return gen.f32_to_bf16_bits(raw.astype(np.float32)).reshape(wl.heads, rows, wl.dim_v)
+
+
 # ----------------------------------------------------------------- paged / variable-length layouts
 @dataclasses.dataclass(frozen=True)
 class PagedLayout:

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert dsa.dsa_version() == 103
+    assert dsa.dsa_version() == 104
     L = dsa.lib()
     assert L.dsa_status_string(0) == b"ok"
     assert L.dsa_status_string(3) == b"workspace too small"
@@ -206,3 +206,38 @@ def test_indexer_kl_validation():
         dsa.dsa.dsa_forward_kl(d, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, FAKE,
                                ws=FAKE, ws_bytes=1 << 30, stream=0)
     assert e.value.status == dsa.dsa.ERR_INVALID_ARG
+
+
+def test_masked_mha_validation():
+    D = dsa.dsa
+    d = _dims(n_q=64, n_kv=64, topk=16)
+    # unsupported per-head dims, too few rope dims, too long a cache
+    for dd, dn, dvh in ((d, 64, 128), (d, 128, 64), (_dims(n_q=64, n_kv=64, dim_qk=512, dim_v=512), 128, 128),
+                        (_dims(n_q=1, n_kv=70000, q_pos0=69999), 128, 128)):
+        with pytest.raises(dsa.DSAError) as e:
+            D.dsa_masked_mha_attn(dd, dn, dvh, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, stream=0)
+        assert e.value.status in (D.ERR_UNSUPPORTED, D.ERR_INVALID_ARG)
+        assert D.dsa_masked_mha_workspace_size(dd, dn, dvh) == 0
+    # bad scale, misaligned output, null mask
+    for args in ((FAKE, FAKE, 0.0, FAKE), (FAKE, FAKE, 0.1, FAKE + 8), (FAKE, None, 0.1, FAKE)):
+        with pytest.raises(dsa.DSAError) as e:
+            D.dsa_masked_mha_attn(d, 128, 128, args[0], FAKE, FAKE, FAKE, args[1], args[2], args[3], stream=0)
+        assert e.value.status == D.ERR_INVALID_ARG
+    with pytest.raises(dsa.DSAError) as e:
+        D.dsa_mha_decompress(d, 128, 128, FAKE, FAKE, FAKE, 65, FAKE, FAKE, stream=0)   # n_rows > n_kv
+    assert e.value.status == D.ERR_INVALID_ARG
+    with pytest.raises(dsa.DSAError) as e:
+        D.dsa_selection_mask(_dims(n_q=1, n_kv=70000, q_pos0=69999), FAKE, FAKE, stream=0)
+    assert e.value.status == D.ERR_UNSUPPORTED
+
+
+def test_masked_mha_workspace_plan():
+    D = dsa.dsa
+    d = _dims(n_q=4096, n_kv=4096, topk=2048)
+    ws = D.dsa_masked_mha_workspace_size(d, 128, 128)
+    # scores + indices of one 4096-row chunk, the bitmap, and per-head K and V of the 4096 visible rows
+    assert ws == 4096 * 4096 * 4 + 4096 * 2048 * 4 + 128 * 4096 * 4 + 2 * 128 * 4096 * 128 * 2
+    with pytest.raises(dsa.DSAError) as e:
+        D.dsa_masked_mha_forward(d, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE,
+                                 ws=FAKE, ws_bytes=ws - 1, stream=0)
+    assert e.value.status == D.ERR_WORKSPACE
