@@ -293,6 +293,86 @@ def time_decode_paged(torch, dsa, stream, reps=10, warmup=2):
     return res
 
 
+def time_short_prefill(torch, dsa, stream, reps=5, warmup=2):
+    """Short prefill (p4k: 4096 tokens, k = 2048) two ways: the sparse MQA-mode
+    forward (dsa_forward) and the masked MHA mode that simulates it
+    (dsa_masked_mha_forward), plus the masked path's stages through the
+    separate calls."""
+    from synth import workloads as W
+    from synth.device import fill_inputs, fill_mha
+    D = dsa.dsa
+    wl = W.WORKLOADS["p4k"]
+    d = fill_inputs(wl)
+    m = fill_mha(wl)
+    dn, dr, dvh = W.mha_dims(wl)
+    dims = D.Dims.of(wl)
+    B, T, S, k, H = wl.batch, wl.n_q, wl.n_kv, wl.topk, wl.heads
+    st = stream.cuda_stream
+    iargs = (d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"])
+    out = torch.empty((B, T, H, dvh), dtype=torch.int16, device="cuda")
+    lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+    nws = D.dsa_masked_mha_workspace_size(dims, dn, dvh)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    t = Timer(torch, stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = t.event()
+        for _ in range(reps):
+            fn()
+        e1 = t.event()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    masked_ms = timed(lambda: D.dsa_masked_mha_forward(dims, dn, dvh, *iargs, m["q_mha"], d["kv"], m["w_uk"],
+                                                       m["w_uv"], wl.sm_scale, out, lse, None, ws, nws, stream=st))
+    dims_f, out_f, lse_f, fws, nfws = alloc_forward(torch, wl, dsa)
+    sparse_ms = timed(lambda: D.dsa_forward(dims_f, *iargs, d["q"], d["kv"], wl.sm_scale, out_f, lse_f, None, fws,
+                                            nfws, stream=st))
+    del out_f, lse_f, fws
+    # stages of the masked path
+    sc = torch.empty((B, T, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, T, k), dtype=torch.int32, device="cuda")
+    mask = torch.empty((B, (S + 31) // 32, T), dtype=torch.int32, device="cuda")
+    k_mha = torch.empty((B, H, S, dn), dtype=torch.int16, device="cuda")
+    v_mha = torch.empty((B, H, S, dvh), dtype=torch.int16, device="cuda")
+    calls = {
+        "indexer": lambda: D.dsa_indexer_scores(dims, *iargs, sc, S, stream=st),
+        "topk": lambda: D.dsa_topk(dims, sc, S, idx, stream=st),
+        "selection_mask": lambda: D.dsa_selection_mask(dims, idx, mask, stream=st),
+        "decompress": lambda: D.dsa_mha_decompress(dims, dn, dvh, d["kv"], m["w_uk"], m["w_uv"], S, k_mha, v_mha,
+                                                   stream=st),
+        "masked_attention": lambda: D.dsa_masked_mha_attn(dims, dn, dvh, m["q_mha"], d["kv"], k_mha, v_mha, mask,
+                                                          wl.sm_scale, out, lse, stream=st),
+    }
+    for f in calls.values():
+        f()
+    torch.cuda.synchronize()
+    tot = {name: 0.0 for name in calls}
+    for _ in range(reps):
+        ev = [t.event()]
+        for f in calls.values():
+            f()
+            ev.append(t.event())
+        torch.cuda.synchronize()
+        for j, name in enumerate(calls):
+            tot[name] += ev[j].elapsed_time(ev[j + 1]) / reps
+    attn_flop = 2.0 * wl.causal_pairs() * H * (dn + dr + dvh)
+    dec_flop = 2.0 * B * S * wl.dim_v * H * (dn + dvh)
+    attn_tf = attn_flop / (tot["masked_attention"] / 1e3) / 1e12
+    dec_tf = dec_flop / (tot["decompress"] / 1e3) / 1e12
+    res = {"workload": "p4k: 1 x 4096 prefill, k = 2048, 128 heads; MHA heads 128 + 64 rope, values 128",
+           "masked_mha_ms": masked_ms, "sparse_mqa_ms": sparse_ms, "speedup_vs_sparse": sparse_ms / masked_ms,
+           "masked_query_tokens_per_s": B * T / (masked_ms / 1e3), "stages_ms": tot,
+           "masked_attention_tflops": attn_tf, "masked_attention_frac": attn_tf / PEAK_BF16_TFLOPS,
+           "masked_attention_flop": attn_flop,
+           "decompress_tflops": dec_tf, "decompress_frac": dec_tf / PEAK_BF16_TFLOPS, "decompress_flop": dec_flop}
+    del d, m, ws, sc, k_mha, v_mha
+    return res
+
+
 def cpu_baseline(wl, n_rows):
     """The CPU oracle (unchanged) on a stratified sample of query rows:
     rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
@@ -442,6 +522,13 @@ def main():
         log(f"[bench] quantise {quant}")
         torch.cuda.empty_cache()
 
+    short = None
+    if not args.no_decode:
+        log("[bench] short prefill p4k: sparse MQA forward vs masked MHA mode")
+        short = time_short_prefill(torch, dsa, stream)
+        log(f"[bench] short prefill {short}")
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_rows} rows")
@@ -457,7 +544,7 @@ def main():
                    "dim_v": wl.dim_v},
         "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
         "topk_GB_per_s": topk_gbs, "roofline": roof, "train_forward_kl": train, "decode": decode,
-        "decode_paged": decode_paged,
+        "decode_paged": decode_paged, "short_prefill": short,
         "quantize": quant, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
