@@ -237,27 +237,29 @@ struct MhaCfg {
 template <int PV>
 __device__ __forceinline__ int swz_v(int r) { return PV == 16 ? 4 * (r & 3) : 0; }
 
+// QK A operand of K step ks: logical piece 2 ks + half of key row `col`
+// (per-head key dims first, then the rope dims).
 template <int DN, int DR, int DVH>
-__device__ __forceinline__ v16f mha_qk(const uint16_t* tile, const v8bf (&qb)[(DN + DR) / 16]) {
+__device__ __forceinline__ v8bf mha_load_a(const uint16_t* tile, int ks, int half, int col) {
   using C = MhaCfg<DN, DR, DVH>;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, col = lane & 31;
-  auto load_a = [&](int ks) {
-    const int p = 2 * ks + half;
-    if (2 * ks < C::kPK) return *(const v8bf*)(tile + (col * C::kPK + (p ^ swz16<C::kPK>(col))) * 8);
-    const int pr = p - C::kPK;
-    return *(const v8bf*)(tile + C::kOffR + (col * C::kPR + (pr ^ swz16<C::kPR>(col))) * 8);
-  };
-  // S^T accumulates in a VGPR tuple (inline asm, next to the softmax that
-  // reads it); the wait states before its first VALU read are explicit.
+  const int p = 2 * ks + half;
+  if (2 * ks < C::kPK) return *(const v8bf*)(tile + (col * C::kPK + (p ^ swz16<C::kPK>(col))) * 8);
+  const int pr = p - C::kPK;
+  return *(const v8bf*)(tile + C::kOffR + (col * C::kPR + (pr ^ swz16<C::kPR>(col))) * 8);
+}
+
+// S^T chain over K steps, the first three A operands already loaded.  The
+// accumulator is a VGPR tuple (inline asm, next to the softmax that reads
+// it); the wait states before its first VALU read are explicit.
+template <int DN, int DR, int DVH>
+__device__ __forceinline__ v16f mha_qk(const uint16_t* tile, v8bf (&abuf)[3], const v8bf (&qb)[(DN + DR) / 16],
+                                       int half, int col) {
+  using C = MhaCfg<DN, DR, DVH>;
   v16f st;
-  v8bf abuf[3];
-#pragma unroll
-  for (int j = 0; j < 3 && j < C::kKS; ++j) abuf[j] = load_a(j);
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
     const v8bf cur = abuf[ks % 3];
-    if (ks + 3 < C::kKS) abuf[ks % 3] = load_a(ks + 3);
+    if (ks + 3 < C::kKS) abuf[ks % 3] = mha_load_a<DN, DR, DVH>(tile, ks + 3, half, col);
     if (ks == 0)
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(cur), "v"(qb[ks]));
     else
@@ -266,6 +268,10 @@ __device__ __forceinline__ v16f mha_qk(const uint16_t* tile, const v8bf (&qb)[(D
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(st));
   return st;
 }
+
+// Copies per wave of one tile region of n DMA instructions: wave w issues
+// instructions w, w + 4, ...
+__host__ __device__ constexpr int dma_share(int n, int w) { return n > w ? (n - w + 3) / 4 : 0; }
 
 template <int DN, int DR, int DVH>
 __global__ void __launch_bounds__(256, 2) masked_mha_kernel(MhaArgs a) {
@@ -314,42 +320,53 @@ __global__ void __launch_bounds__(256, 2) masked_mha_kernel(MhaArgs a) {
   const uint16_t* vhb = a.vh + ((int64_t)b * a.H + h) * a.S_h * DVH;
   const uint16_t* kvb = a.kv + (int64_t)b * a.S * a.Dk + a.Dv;
   const uint32_t* mb = a.mask + (int64_t)b * a.NC * a.T;
-  const int nd = (C::kDma - wave + 3) / 4;       // this wave's DMA instructions per chunk
+  // This wave's DMA instructions per chunk (the same for every chunk).
+  const int nd = dma_share(C::kDmaK, wave) + dma_share(C::kDmaR, wave) + dma_share(C::kDmaV, wave) +
+                 dma_share(C::kDmaM, wave);
 
   // Rows past the block's last position are clamped to it (finite data,
   // masked out below).  Every copy takes a wave-uniform base in SGPRs and a
   // 32-bit byte offset per lane (a head's K_h / V_h block, a sequence's
-  // latent cache and its mask are each below 4 GiB).
+  // latent cache and its mask are each below 4 GiB).  Wave w issues
+  // instructions w, w + 4, ... of every region, so the addresses are
+  // compile-time offsets from a few per-lane bases.
   auto gather = [&](int c, uint16_t* tl) {
     const int s0 = 32 * c;
 #pragma unroll
-    for (int jj = 0; jj < (C::kDma + 3) / 4; ++jj) {
-      const int j = jj * 4 + wave;
-      if (j >= C::kDma) break;
-      if (j < C::kDmaK) {
+    for (int i = 0; i < (C::kDmaK + 3) / 4; ++i) {
+      const int j = wave + 4 * i;
+      if ((C::kDmaK % 4) == 0 || j < C::kDmaK) {
         const int q = j * 64 + lane, r = q / C::kPK, pp = q % C::kPK;
         const uint32_t s = (uint32_t)min(s0 + r, p_last);
         dma_x4_s((s * DN + 8 * (pp ^ swz16<C::kPK>(r))) * 2u, khb, lds_addr(tl + j * 512));
-      } else if (j < C::kDmaK + C::kDmaR) {
-        const int j2 = j - C::kDmaK;
-        const int q = j2 * 64 + lane, r = q / C::kPR, pp = q % C::kPR;
-        const uint32_t s = (uint32_t)min(s0 + r, p_last);
-        dma_x4_s((s * (uint32_t)a.Dk + 8 * (pp ^ swz16<C::kPR>(r))) * 2u, kvb, lds_addr(tl + C::kOffR + j2 * 512));
-      } else if (j < C::kDmaK + C::kDmaR + C::kDmaV) {
-        const int j3 = j - C::kDmaK - C::kDmaR;
-        const int q = j3 * 64 + lane, r = q / C::kPV, pp = q % C::kPV;
-        const uint32_t s = (uint32_t)min(s0 + r, p_last);
-        dma_x4_s((s * DVH + 8 * (pp ^ swz_v<C::kPV>(r))) * 2u, vhb, lds_addr(tl + C::kOffV + j3 * 512));
-      } else {
-        const int j4 = j - C::kDmaK - C::kDmaR - C::kDmaV;
-        const uint32_t tq = (uint32_t)min(t0 + 64 * j4 + lane, a.T - 1);
-        dma_x1_s(((uint32_t)c * (uint32_t)a.T + tq) * 4u, mb, lds_addr(tl + C::kOffM + j4 * 128));
       }
+    }
+#pragma unroll
+    for (int i = 0; i < (C::kDmaR + 3) / 4; ++i) {
+      const int j = wave + 4 * i;
+      if ((C::kDmaR % 4) == 0 || j < C::kDmaR) {
+        const int q = j * 64 + lane, r = q / C::kPR, pp = q % C::kPR;
+        const uint32_t s = (uint32_t)min(s0 + r, p_last);
+        dma_x4_s((s * (uint32_t)a.Dk + 8 * (pp ^ swz16<C::kPR>(r))) * 2u, kvb, lds_addr(tl + C::kOffR + j * 512));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (C::kDmaV + 3) / 4; ++i) {
+      const int j = wave + 4 * i;
+      if ((C::kDmaV % 4) == 0 || j < C::kDmaV) {
+        const int q = j * 64 + lane, r = q / C::kPV, pp = q % C::kPV;
+        const uint32_t s = (uint32_t)min(s0 + r, p_last);
+        dma_x4_s((s * DVH + 8 * (pp ^ swz_v<C::kPV>(r))) * 2u, vhb, lds_addr(tl + C::kOffV + j * 512));
+      }
+    }
+    if (wave < C::kDmaM) {
+      const uint32_t tq = (uint32_t)min(t0 + 64 * wave + lane, a.T - 1);
+      dma_x1_s(((uint32_t)c * (uint32_t)a.T + tq) * 4u, mb, lds_addr(tl + C::kOffM + wave * 128));
     }
   };
 
-  // Transposed V^T operand reads (see the sparse MLA kernel for the lane
-  // mapping): lane group g = lane / 16 covers rows 4 * (g / 2) + jl / 4 of a
+  // Transposed V^T operand reads (the lane mapping of the sparse MLA
+  // kernel): lane group g = lane / 16 covers rows 4 * (g / 2) + jl / 4 of a
   // 4-row block and dims 16 * (g % 2) + 4 * (jl % 4) .. + 3 of a 32-dim tile.
   const int g = lane >> 4, jl = lane & 15;
   const int vrow = 4 * (g >> 1) + (jl >> 2);
@@ -360,6 +377,15 @@ __global__ void __launch_bounds__(256, 2) masked_mha_kernel(MhaArgs a) {
   const int vswz = swz_v<C::kPV>(vrow) >> 2;
   const int v_lo = C::kOffV + vrow * C::kPV * 8 + vpiece * 8 + vsub;
   const int v_hi = v_lo + 8 * C::kPV * 8;
+  constexpr int kM = 2 * C::kNT;             // PV MFMAs per chunk
+  constexpr int kLookV = kM < 4 ? kM : 4;    // PV operands in flight
+  auto load_v = [&](const uint16_t* tl, int m) {
+    const int ti = m >> 1, kk = m & 1;
+    const int off = 16 * kk * C::kPV * 8 + 32 * (ti ^ vswz);
+    const v4bf lo = lds_read_tr16(tl + v_lo + off);
+    const v4bf hi = lds_read_tr16(tl + v_hi + off);
+    return (v8bf)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
   v16f o[C::kNT];
 #pragma unroll
@@ -368,11 +394,19 @@ __global__ void __launch_bounds__(256, 2) masked_mha_kernel(MhaArgs a) {
   const float zscale = a.sm_scale * kLog2e;
 
   auto attend = [&](int c, const uint16_t* tl) {
+    // The mask word and the first QK operands are read together.
     uint32_t word = ((const uint32_t*)(tl + C::kOffM))[32 * wave + col];
+    v8bf abuf[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) abuf[j] = mha_load_a<DN, DR, DVH>(tl, j, half, col);
     const int nv = n_keys - 32 * c;                     // causal keys of this chunk
     if (nv < 32) word &= nv <= 0 ? 0u : ((1u << nv) - 1u);
     if (__builtin_amdgcn_ballot_w64(word != 0u) == 0) return;   // wave-uniform
-    const v16f st = mha_qk<DN, DR, DVH>(tl, qb);
+    const v16f st = mha_qk<DN, DR, DVH>(tl, abuf, qb, half, col);
+    // V^T operands of the first PV MFMAs, in flight during the softmax.
+    v8bf vbuf[kLookV];
+#pragma unroll
+    for (int j = 0; j < kLookV; ++j) vbuf[j] = load_v(tl, j);
     float z[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) z[j] = st[j];
@@ -380,8 +414,9 @@ __global__ void __launch_bounds__(256, 2) masked_mha_kernel(MhaArgs a) {
       const uint32_t vh = word >> (4 * half);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int r = 8 * (j >> 2) + (j & 3);           // key row minus 4 * half
-        if (!((vh >> r) & 1u)) z[j] = -INFINITY;
+        // keep = all ones if key row 8 (j / 4) + j % 4 (+ 4 half) is selected
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)vh, 8 * (j >> 2) + (j & 3), 1);
+        z[j] = __uint_as_float((__float_as_uint(z[j]) & keep) | (0xFF800000u & ~keep));
       }
     }
     float mx = z[0];
@@ -406,13 +441,10 @@ __global__ void __launch_bounds__(256, 2) masked_mha_kernel(MhaArgs a) {
       pb[j >> 3][j & 7] = (__bf16)pj;
     }
 #pragma unroll
-    for (int m = 0; m < 2 * C::kNT; ++m) {
-      const int ti = m >> 1, kk = m & 1;
-      const int off = 16 * kk * C::kPV * 8 + 32 * (ti ^ vswz);
-      const v4bf lo = lds_read_tr16(tl + v_lo + off);
-      const v4bf hi = lds_read_tr16(tl + v_hi + off);
-      const v8bf vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[ti] = mfma_bf16_32x32x16(vop, pb[kk], o[ti]);
+    for (int m = 0; m < kM; ++m) {
+      const v8bf cur = vbuf[m % kLookV];
+      if (m + kLookV < kM) vbuf[m % kLookV] = load_v(tl, m + kLookV);
+      o[m >> 1] = mfma_bf16_32x32x16(cur, pb[m & 1], o[m >> 1]);
     }
   };
 
