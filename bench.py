@@ -411,6 +411,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=1)
+    ap.add_argument("--short-prefill-only", action="store_true",
+                    help="run only the short-prefill comparison (4K tokens: masked MHA mode vs sparse MQA) "
+                         "and print its JSON; for profiling those kernels alone")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel that "
                          "calibrates FETCH_SIZE/WRITE_SIZE counters in a rocprofv3 --pmc run)")
@@ -436,6 +439,10 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {n} bytes done")
         del src, dst
+    if args.short_prefill_only:
+        print(json.dumps({"short_prefill": time_short_prefill(torch, dsa, stream, reps=max(args.steps, 1),
+                                                              warmup=args.warmup)}), flush=True)
+        return
     log(f"[bench] filling {wl.name} inputs on the GPU")
     d = fill_inputs(wl)
     torch.cuda.synchronize()
