@@ -51,6 +51,8 @@ CASES = {
     "batch2": W.custom("p4k", batch=2, n_q=96, n_kv=2196, q_pos0=2100, heads=8),
     # sparse selections (64 of ~600 keys): most chunks hold no selected key
     "small_k": W.custom("p4k", n_q=130, n_kv=700, q_pos0=570, topk=64, heads=8),
+    # small dims, three sequences, 77 ragged rows continuing a prefill at position 179
+    "tiny_b3": W.custom("tiny", batch=3, n_q=77, q_pos0=179),
 }
 
 
@@ -223,7 +225,7 @@ def test_masked_mha_dense_and_empty_masks():
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
-@pytest.mark.parametrize("name", ["tiny", "p4k_deep", "small_k"])
+@pytest.mark.parametrize("name", ["tiny", "p4k_deep", "small_k", "batch2", "tiny_b3"])
 def test_masked_mha_forward_bitwise_and_end_to_end(name):
     wl = CASES[name]
     mh = MhaHost(wl)
