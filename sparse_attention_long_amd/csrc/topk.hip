@@ -5,19 +5,26 @@
 // lower index).
 //
 // One workgroup of 1024 threads per row.  Scores are mapped to
-// order-preserving 32-bit keys (NaN lowest, -0 == +0) and the m-th largest
-// key tau is found by a radix select with 13/10/9-bit digits:
-//   pass 1 (memory): LDS histogram of the top 13 bits (sign, exponent and 4
-//          mantissa bits) -> bin b1 holding tau;
-//   pass 2 (memory, mostly the Infinity Cache): keys above bin b1 are marked
-//          in an LDS bitmap, keys inside bin b1 are appended (one atomic per
-//          wave) to an LDS candidate list;
-//   digits 2 and 3 are resolved on the candidates in LDS.
-// If bin b1 holds more keys than the candidate list can, digits 2 and 3 take
-// two more passes over the row instead.  Keys above tau go into the bitmap,
-// keys equal to tau into a tie bitmap; the first (m - #above) ties in index
-// order are kept and the bitmap is emitted in ascending order with a
-// block-wide popcount prefix sum.  The selection needs no sort.
+// order-preserving 32-bit keys (NaN lowest, -0 == +0); tau, the m-th largest
+// key, is found as follows.
+//   Sampled single pass (the usual path): 2048 scores (32 blocks of 64
+//          spread over the row) give a provisional cutoff lo, the lower
+//          edge of the 13-bit bin (sign, exponent, 4 mantissa bits) that
+//          holds the sample's rank-r key, with r set so that about 2m keys
+//          of the row are expected at or above lo.  One pass over the row
+//          appends every key >= lo, with its index, to an LDS candidate list
+//          (one LDS atomic per wave per iteration; ballots give the slots).
+//          If between m and `cap` keys were collected, tau is among them:
+//          its 13-bit bin, then the 10- and 9-bit digits, are resolved on
+//          the candidates in LDS.
+//   Fallback (the sample missed): pass 1 builds the LDS histogram of the
+//          13-bit digit over the whole row and fixes tau's bin b1; pass 2
+//          marks the keys above b1 and collects bin b1 into the candidate
+//          list; a bin wider than the list takes one more pass per digit.
+// Keys above tau go into a selection bitmap and keys equal to tau into a
+// tie bitmap; the first (m - #above) ties in index order are kept, and the
+// bitmap is emitted in ascending order with a block-wide popcount prefix
+// sum.  The selection needs no sort.
 //
 // The row is streamed with 16-byte loads, four per thread in flight (64 KB
 // per workgroup), after a scalar head that reaches 16-byte alignment.
