@@ -373,6 +373,40 @@ def time_short_prefill(torch, dsa, stream, reps=5, warmup=2):
     return res
 
 
+def roofline_sum(wl, ms):
+    """Lower bound on the forward step from the three stages' rooflines:
+    indexer FP8 work, top-k bytes, and the larger of the attention's BF16
+    work and its q/out bytes, at the published peaks."""
+    P, Q = wl.causal_pairs(), wl.selected_pairs()
+    L = wl.batch * wl.n_q
+    t_idx = 2.0 * P * wl.idx_heads * wl.idx_dim / (PEAK_FP8_TFLOPS * 1e12)
+    t_topk = (4.0 * P + 4.0 * L * wl.topk) / (PEAK_HBM_GBS * 1e9)
+    qo_bytes = 2.0 * L * wl.heads * (wl.dim_qk + wl.dim_v)
+    t_attn = max(2.0 * Q * wl.heads * (wl.dim_qk + wl.dim_v) / (PEAK_BF16_TFLOPS * 1e12), qo_bytes / (PEAK_HBM_GBS * 1e9))
+    t_star = (t_idx + t_topk + t_attn) * 1e3
+    return {"t_star_ms": t_star, "indexer_ms": t_idx * 1e3, "topk_ms": t_topk * 1e3, "attention_ms": t_attn * 1e3,
+            "frac": t_star / ms, "query_tokens_per_s_at_roof": L / (t_star / 1e3)}
+
+
+def hbm_copy_rate(torch, mib=1024, reps=5):
+    """Achievable HBM rate on this machine: a plain device-to-device copy of
+    `mib` MiB (read + write bytes per second)."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * n / (e0.elapsed_time(e1) / reps / 1e3) / 1e9
+    del src, dst
+    return {"GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "bytes_copied": n}
+
+
 def cpu_baseline(wl, n_rows):
     """The CPU oracle (unchanged) on a stratified sample of query rows:
     rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
@@ -552,7 +586,8 @@ def main():
         "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
         "topk_GB_per_s": topk_gbs, "roofline": roof, "train_forward_kl": train, "decode": decode,
         "decode_paged": decode_paged, "short_prefill": short,
-        "quantize": quant, "cpu_baseline": cpu,
+        "quantize": quant, "cpu_baseline": cpu, "roofline_sum": roofline_sum(wl, ms),
+        "hbm_copy": hbm_copy_rate(torch),
     }
     print(json.dumps(res), flush=True)
 
