@@ -120,7 +120,9 @@ int attn_nsplit(const dsa_dims* d) {
 size_t attn_partial_bytes(const dsa_dims* d, int64_t rows_per_seq) {
   const int ns = attn_nsplit(d);
   if (ns <= 1) return 0;
-  return (size_t)d->batch * rows_per_seq * ns * d->heads * ((size_t)d->dim_v + 1) * sizeof(float);
+  // bf16 partial outputs, then one f32 log-sum-exp per (row, split, head)
+  const size_t n = (size_t)d->batch * rows_per_seq * ns * d->heads;
+  return (n * d->dim_v * sizeof(uint16_t) + 15) / 16 * 16 + n * sizeof(float);
 }
 
 // Query rows per chunk of dsa_forward: keep a chunk's scores near 128 MB.
@@ -272,8 +274,10 @@ int attn_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, cons
   a.lse = lse;
   a.nsplit = attn_nsplit(d);
   const size_t rows_total = (size_t)d->batch * d->n_q;
-  a.part_o = (float*)ws;
-  a.part_lse = a.nsplit > 1 ? (float*)ws + rows_total * a.nsplit * d->heads * d->dim_v : nullptr;
+  a.part_o = (uint16_t*)ws;
+  a.part_lse = a.nsplit > 1
+                   ? (float*)((char*)ws + (rows_total * a.nsplit * d->heads * d->dim_v * sizeof(uint16_t) + 15) / 16 * 16)
+                   : nullptr;
   a.qrows_b = d->n_q;
   a.idx_rows_b = d->n_q;
   a.B = d->batch;
@@ -345,8 +349,11 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     aa.out = out + i0 * d->heads * d->dim_v;
     aa.lse = lse ? lse + i0 * d->heads : nullptr;
     aa.nsplit = nsplit;
-    aa.part_o = (float*)(wsb + L.part_off);
-    aa.part_lse = nsplit > 1 ? aa.part_o + (size_t)d->batch * rows * nsplit * d->heads * d->dim_v : nullptr;
+    aa.part_o = (uint16_t*)(wsb + L.part_off);
+    aa.part_lse =
+        nsplit > 1
+            ? (float*)((char*)aa.part_o + ((size_t)d->batch * rows * nsplit * d->heads * d->dim_v * sizeof(uint16_t) + 15) / 16 * 16)
+            : nullptr;
     aa.qrows_b = d->n_q;
     aa.B = d->batch;
     aa.rows = rows;

@@ -72,7 +72,7 @@ struct AttnArgs {
   const int32_t* idx;     // [B, idx_rows_b, k]
   uint16_t* out;          // [B, qrows_b, H, Dv] bf16
   float* lse;             // [B, qrows_b, H] or null
-  float* part_o;          // split partials [B*rows, nsplit, H, Dv] f32 (nsplit > 1)
+  uint16_t* part_o;       // split partials [B*rows, nsplit, H, Dv] bf16, each normalised (nsplit > 1)
   float* part_lse;        // [B*rows, nsplit, H]
   int64_t qrows_b;        // row stride between sequences for q, out, lse
   int64_t idx_rows_b;     // row stride between sequences for idx

@@ -85,7 +85,7 @@ def test_attention_validation_and_workspace():
     # decode-like shapes split the selected set and need a workspace
     d = _dims(batch=64, n_q=1, n_kv=131072, q_pos0=131071, topk=2048)
     need = dsa.dsa_attn_workspace_size(d)
-    assert need == 64 * 4 * 128 * 513 * 4
+    assert need == 64 * 4 * 128 * (512 * 2 + 4)   # bf16 partial outputs + f32 log-sum-exp
     with pytest.raises(dsa.DSAError) as e:
         dsa.dsa_sparse_mla_attn(d, FAKE, FAKE, FAKE, 0.1, FAKE, ws=FAKE, ws_bytes=need - 1, stream=0)
     assert e.value.status == dsa.dsa.ERR_WORKSPACE
