@@ -256,40 +256,32 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
     const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
     find_bin(hist, kBins1, r, sh);
     const uint32_t lo = sh.bin << kShift1;
-    // key(x) >= lo as one float compare: lo is a bin edge of the order
-    // key, and the float whose key is lo (or -inf below the finite range)
-    // orders the same way; NaN (key 0) fails it.  lo = 0 (every key,
-    // NaN included) is left to the exact radix passes below.
-    const float flo = lo >= 0x80000000u ? __uint_as_float(lo & 0x7FFFFFFFu)
-                      : lo <= 0x007FFFFFu ? -INFINITY : __uint_as_float(~lo);
     for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
-    if (lo != 0u) {   // block-uniform
+    {
       // One wave-level append per iteration: each lane marks its candidates
       // among its 4 x 4 scores, the wave forms the prefix of the counts from
-      // ballots, and one LDS atomic reserves the wave's slots.  The next
-      // iteration's loads are issued before this one's scores are examined.
+      // ballots, and one LDS atomic reserves the wave's slots.
       const int lane = t & 63;
       const int iters = (row.nq + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-      float4 v[kUnroll], nv[kUnroll];
-      auto load = [&](int it, float4 (&dst)[kUnroll]) {
+      for (int it = 0; it < iters; ++it) {
+        float4 v[kUnroll];
+        bool ok[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int q = (it * kUnroll + u) * kThreads + t;
-          dst[u] = row.xv[q < row.nq ? q : 0];
+          ok[u] = q < row.nq;
+          v[u] = row.xv[ok[u] ? q : 0];
         }
-      };
-      if (iters > 0) load(0, v);
-      for (int it = 0; it < iters; ++it) {
-        if (it + 1 < iters) load(it + 1, nv);
+        uint32_t keys[4 * kUnroll];
         uint32_t cm = 0;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          // past the row: a NaN threshold fails every compare
-          const float thr = (it * kUnroll + u) * kThreads + t < row.nq ? flo : __builtin_nanf("");
-          cm |= (v[u].x >= thr ? 1u : 0u) << (4 * u + 0);
-          cm |= (v[u].y >= thr ? 1u : 0u) << (4 * u + 1);
-          cm |= (v[u].z >= thr ? 1u : 0u) << (4 * u + 2);
-          cm |= (v[u].w >= thr ? 1u : 0u) << (4 * u + 3);
+          keys[4 * u + 0] = order_key(v[u].x);
+          keys[4 * u + 1] = order_key(v[u].y);
+          keys[4 * u + 2] = order_key(v[u].z);
+          keys[4 * u + 3] = order_key(v[u].w);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) cm |= (ok[u] && keys[4 * u + c] >= lo ? 1u : 0u) << (4 * u + c);
         }
         uint32_t total;
         const uint32_t pre = wave_prefix_small((uint32_t)__popc(cm), total);
@@ -303,17 +295,13 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
           for (int j = 0; j < 4 * kUnroll; ++j) {
             if ((cm >> j) & 1u) {
               if (pos < (uint32_t)cap) {
-                const float4 w4 = v[j >> 2];
-                const float x = (j & 3) == 0 ? w4.x : (j & 3) == 1 ? w4.y : (j & 3) == 2 ? w4.z : w4.w;
-                ckey[pos] = order_key(x);
+                ckey[pos] = keys[j];
                 cidx[pos] = (uint32_t)(row.h + 4 * ((it * kUnroll + (j >> 2)) * kThreads + t) + (j & 3));
               }
               ++pos;
             }
           }
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = nv[u];
       }
       auto tail = [&](int e) {
         const uint32_t key = order_key(row.x[e]);
