@@ -130,6 +130,7 @@ int64_t forward_chunk_rows(const dsa_dims* d) {
   const int64_t budget = 128ll << 20;
   int64_t tc = budget / ((int64_t)d->batch * d->n_kv * 4);
   if (tc >= 64) tc = tc / 32 * 32;
+  if (tc > 1) tc &= ~(int64_t)1;   // even: a row keeps its indexer slot parity in every chunk
   if (tc < 1) tc = 1;
   if (tc > d->n_q) tc = d->n_q;
   return tc;

@@ -35,6 +35,17 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
 }
 
+// The same MFMA with E8M0 block scales for A (bits 7..0 of sa, value
+// 2^(sa - 127)).  Measured on gfx950: the scale held by lane 16*sb + rho
+// multiplies, in A row rho, bytes [16*(sb/2), 16*(sb/2) + 16) of the lanes
+// 16*(2*(sb%2)) + rho and 16*(2*(sb%2) + 1) + rho.  In terms of the byte
+// index k = 32*(l/16) + j of the layout above, block sb is the set of k
+// with 2*((k%32)/16) + k/64 == sb.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_sa(const v8i& a, int sa, const v8i& b) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, sa, 0, 127);
+}
+
 // 32x32x16 bf16 MFMA.  Lane l holds row (A) / column (B) l%32 and K elements
 // [8*(l/32), 8*(l/32)+8); the result element j of lane l is row
 // 8*(j/4) + 4*(l/32) + j%4 of column l%32.
@@ -76,6 +87,11 @@ __device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
 
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float max_rows16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 

@@ -14,13 +14,32 @@
 // lane holds 4 heads of one key per instruction, and the remaining sum over
 // the four 16-lane rows is a reduce-scatter with two permlane swaps.
 //
-// Two work shapes share the per-tile arithmetic (so they give bit-identical
-// scores):
-//  * prefill: a wave keeps the A operands (q) of 4 query rows in registers
-//    and streams 16-key tiles; the 4 rows' partials are reduce-scattered so
-//    each 16-lane row ends with one query's 16 scores.
+// The ReLU is split as ReLU(x) = (|x| + x) / 2.  With the folded weights
+// w'[j] = w[t,j]*qs[t]/2,
+//
+//   I[t,s] / ks[s] = sum_j w'[j] |d_j| + sum_j w'[j] d_j,   d_j = qhat[t,j] . khat[s],
+//
+// where the first sum is one fma per head (the abs is a free source
+// modifier) and the second is linear in the key: v[t] . khat[s] with
+// v[t] = sum_j w'[j] qhat[t,j].  Per query row, v is split into e4m3
+// residual levels (kLinLevels of them, each with an E8M0 scale per MFMA
+// scale block of 32 values, each level leaving at most 1/16 of the previous
+// residual), and one extra MFMA per key tile yields every level's dot
+// product.  That halves the VALU work per score.  Each wave then issues a
+// step's MFMAs back to back and its epilogue after them, so the two waves
+// on a SIMD alternate between the matrix core and the VALU.
+//
+// Two work shapes:
+//  * prefill: a wave keeps the A operands (q) of 2 query rows in registers
+//    and streams pairs of 16-key tiles; the 4 (row, tile) partials are
+//    reduce-scattered so each 16-lane row ends with 16 scores of one query.
+//    Both prefill kernels (keys staged in LDS, or read directly for paged
+//    caches and d_I < 128) share the per-tile arithmetic above and give
+//    bit-identical scores.
 //  * decode: a wave keeps one row's q and streams 4 key tiles per step; the
-//    reduce-scatter leaves 64 consecutive keys' scores, one per lane.
+//    reduce-scatter leaves 64 consecutive keys' scores, one per lane.  A
+//    wave sees only 512 keys, too few to pay for the level tile's set-up,
+//    so this form applies the ReLU directly (same value, other rounding).
 #include <climits>
 
 #include "dsa_device.h"
@@ -114,9 +133,9 @@ struct KeyStream {
   }
 };
 
-// Folded head weights w[t,j]*qs[t] for the 4 heads (per head tile) this lane
-// sees in the MFMA result: head 16*ht + 4*(lane/16) + r.
-__device__ __forceinline__ void load_weights(const IndexerArgs& a, int b, int i, int lane,
+// Folded head weights w[t,j]*qs[t]*fold for the 4 heads (per head tile)
+// this lane sees in the MFMA result: head 16*ht + 4*(lane/16) + r.
+__device__ __forceinline__ void load_weights(const IndexerArgs& a, int b, int i, int lane, float fold,
                                              float (&wq)[kMaxHeadTiles][4]) {
   // Branch-free: clamped indices, then masks, so all loads are in flight at once.
   const bool row_ok = i < a.rows;
@@ -129,7 +148,7 @@ __device__ __forceinline__ void load_weights(const IndexerArgs& a, int b, int i,
     for (int r = 0; r < 4; ++r) {
       const int h = 16 * ht + 4 * (lane >> 4) + r;
       const float wv = bf16_to_f32(wr[min(h, a.HI - 1)]);
-      wq[ht][r] = (row_ok && h < a.HI) ? wv * qs : 0.f;
+      wq[ht][r] = (row_ok && h < a.HI) ? wv * qs * fold : 0.f;
     }
 }
 
@@ -138,20 +157,20 @@ __device__ __forceinline__ void load_weights(const IndexerArgs& a, int b, int i,
 // first canonicalise the MFMA result (one more VALU op per element).
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Four partial head sums: for u = 0..3, the MFMA products of query operand
-// set qa[u] (NHT head tiles) with key tile kt[u], followed by this lane's
-// sum_h wq[u][h] * ReLU(dot) in the fixed order ht = 0..NHT-1, r = 0..3.
-// The MFMAs are issued head-tile-major and each result's epilogue runs four
-// MFMAs after it was issued, so the matrix core and the VALU work overlap
-// within one wave (1 MFMA : 8 VALU is the balanced ratio for this tile).
+// Decode form: one query row and four key tiles; for u = 0..3 this lane's
+// share of sum_h wq[h] * ReLU(qhat_h . khat) for key tile kt[u], in the
+// fixed order ht = 0..NHT-1, r = 0..3.  With few keys per wave the level
+// tile of the prefill form would not pay for its set-up, so this form
+// keeps the ReLU (weights folded as w[t,j]*qs[t]).  Each result's epilogue
+// runs four MFMAs after it was issued (1 MFMA : 8 VALU).
 template <int NHT>
-__device__ __forceinline__ void tile_partials(const v8i* const (&qa)[4], const float (*const (&wq)[4])[4],
-                                              const v8i* const (&kt)[4], float (&acc)[4]) {
+__device__ __forceinline__ void tile_partials_relu(const v8i* qa, const float (*wq)[4], const v8i* const (&kt)[4],
+                                                   float (&acc)[4]) {
   v4f d[NHT][4];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) d[ht][u] = mfma_fp8_16x16x128(qa[u][ht], *kt[u]);
+    for (int u = 0; u < 4; ++u) d[ht][u] = mfma_fp8_16x16x128(qa[ht], *kt[u]);
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = 0.f;
 #pragma unroll
@@ -159,9 +178,7 @@ __device__ __forceinline__ void tile_partials(const v8i* const (&qa)[4], const f
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[u] = fmaf(wq[u][ht][r], relu_bits(d[ht][u][r]), acc[u]);
-  // schedule: pending LDS reads (the next step's operands, if any) first,
-  // then 4 MFMAs, then (1 MFMA, 8 VALU) pairs, then the tail
+      for (int r = 0; r < 4; ++r) acc[u] = fmaf(wq[ht][r], relu_bits(d[ht][u][r]), acc[u]);
   __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
 #pragma unroll
   for (int k = 0; k < 4 && k < 4 * NHT; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -171,6 +188,190 @@ __device__ __forceinline__ void tile_partials(const v8i* const (&qa)[4], const f
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+}
+
+// ---- Prefill form: the ReLU split and the level tile ----
+//
+// The extra MFMA's A operand has 16 rows = 2 slots x 8 levels: row
+// rho = 4*G + j (G = rho/4, j = rho%4) is slot j/2, level 2*G + j%2.  A
+// result lane in 16-lane row G thus holds, for its key, levels 2G and 2G+1
+// of slot 0 (elements 0, 1) and of slot 1 (elements 2, 3); the reduce-scatter
+// over the four rows that already sums the head partials also sums the
+// levels.  Levels kLinLevels..7 are zero rows.  Query row i of a prefill
+// span takes slot i % 2 (waves start at even rows), in both prefill kernels.
+constexpr int kLinLevels = 6;
+constexpr int kLinScratch = 2 * 8 * 128 + 2 * 8 * 4;   // LDS per wave: codes [slot][level][128 B], E8M0 [slot][level][4]
+
+struct LinOp {
+  v8i a;    // codes of row lane%16, K bytes [32*(lane/16), +32)
+  int sc;   // their E8M0 block scale
+};
+
+// Inputs of v for the query rows of the two slots: lane l loads, for heads
+// 8*i + l/8, the 16 code bytes [16*(l%8), +16) and the folded weight.  All
+// loads are issued here at once, ahead of the q tiles, so that their
+// latency overlaps; a slot whose row lies outside [0, rows) loads zeros.
+template <int NHT>
+struct LinLoads {
+  u32x4 x[2][2 * NHT];
+  float wv[2][2 * NHT];
+};
+
+template <int NHT>
+__device__ __forceinline__ void lin_load(const IndexerArgs& a, int b, int r0, int r1, int lane, LinLoads<NHT>& ld) {
+  const int c = lane & 7, e = lane >> 3;   // 16-byte chunk of K, head group
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    const int i = sl ? r1 : r0;
+    const bool row_ok = i >= 0 && i < a.rows;
+    const int64_t row = (int64_t)b * a.qrows_b + min(max(i, 0), a.rows - 1);
+    const float qs = row_ok ? a.q_scale[row] : 0.f;
+#pragma unroll
+    for (int i8 = 0; i8 < 2 * NHT; ++i8) {
+      const int h = 8 * i8 + e;
+      const bool ok = row_ok && h < a.HI;
+      const int hc = min(h, a.HI - 1);
+      const float w = bf16_to_f32(a.w[row * a.HI + hc]);
+      ld.wv[sl][i8] = ok ? w * qs * 0.5f : 0.f;
+      ld.x[sl][i8] = load16_or_zero(a.q_idx + (row * a.HI + hc) * a.dI, 16 * c, a.dI, ok);
+    }
+  }
+}
+
+// v of slot sl, partly reduced.  Lane l first sums its heads 8*i + l/8
+// over 16 values of K, then the sums are combined over lane bits 5 and 4:
+// lane l ends with the sum over the heads j with j % 2 == (l/8) % 2, for
+// k = 16*(l%8) + 4*(l/16) + t, t = 0..3.  Lanes l and l^8 hold the two
+// halves of each total.
+template <int NHT>
+__device__ __forceinline__ void lin_half_sums(const LinLoads<NHT>& ld, int sl, float (&out)[4]) {
+  float p[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) p[t] = 0.f;
+#pragma unroll
+  for (int i8 = 0; i8 < 2 * NHT; ++i8) {
+    const float wv = ld.wv[sl][i8];
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ld.x[sl][i8][dw], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ld.x[sl][i8][dw], true);
+      p[4 * dw + 0] = fmaf(wv, lo[0], p[4 * dw + 0]);
+      p[4 * dw + 1] = fmaf(wv, lo[1], p[4 * dw + 1]);
+      p[4 * dw + 2] = fmaf(wv, hi[0], p[4 * dw + 2]);
+      p[4 * dw + 3] = fmaf(wv, hi[1], p[4 * dw + 3]);
+    }
+  }
+  // sum over lane bit 5 (p[t] stays in lanes < 32, p[t+8] in lanes >= 32),
+  // then over bit 4 (rows 0, 2 keep the first four, rows 1, 3 the last four)
+  float r1[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r1[t] = reduce_halves(p[t], p[t + 8]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) out[t] = reduce_rows16(r1[t], r1[t + 4]);
+}
+
+// Level-tile operand from the loads of lin_load (slot 0: row r0, slot 1:
+// row r1).  `scratch` is kLinScratch bytes of LDS owned by this wave
+// (16-byte aligned).
+template <int NHT>
+__device__ __forceinline__ LinOp lin_operand(const LinLoads<NHT>& ld, int lane, uint8_t* scratch) {
+  float h0[4], h1[4];
+  lin_half_sums<NHT>(ld, 0, h0);
+  lin_half_sums<NHT>(ld, 1, h1);
+  // Sum over lane bit 3, keeping slot 0 in lanes with bit 3 clear and slot
+  // 1 in the others: lane l then holds v[slot][16*(l%8) + 4*(l/16) + t].
+  const bool odd = (lane & 8) != 0;
+  float v[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float keep = odd ? h1[t] : h0[t], send = odd ? h0[t] : h1[t];
+    v[t] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0x128, 0xF, 0xF, false));   // row_ror:8
+  }
+  const int slot = odd ? 1 : 0;
+  uint32_t* codes = (uint32_t*)scratch;        // [slot][level][32 dwords]
+  uint8_t* scl = scratch + 2 * 8 * 128;        // [slot][level][4 blocks]
+  const int dw = 4 * (lane & 7) + (lane >> 4);   // dword holding k = 16*(l%8) + 4*(l/16) + 0..3
+  // Its MFMA scale block: block sb holds the k with 2*((k%32)/16) + k/64 == sb,
+  // and the scale of (row rho, sb) comes from lane 16*sb + rho.
+  const int blk = 2 * (lane & 1) + ((lane >> 2) & 1);
+#pragma unroll
+  for (int lev = 0; lev < 8; ++lev) {
+    uint32_t code = 0u, e8 = 127u;
+    if (lev < kLinLevels) {
+      // block max over the 8 lanes of (slot, block): lane bits 1, 4 and 5
+      float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+      mx = max_halves(max_rows16(mx));
+      // scale 2^(E-7-127): the block max lands in [128, 256), below the e4m3 limit
+      const uint32_t E = __float_as_uint(mx) >> 23;
+      const bool zero = E < 30u;   // nothing left worth a level (below 2^-97)
+      e8 = zero ? 127u : E - 7u;
+      const float down = zero ? 0.f : __uint_as_float((261u - E) << 23);
+      const float up = zero ? 0.f : __uint_as_float((E - 7u) << 23);
+      int c2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * down, v[1] * down, 0, false);
+      c2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * down, v[3] * down, c2, true);
+      const auto q01 = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
+      const auto q23 = __builtin_amdgcn_cvt_pk_f32_fp8(c2, true);
+      // the residual is exact: the level value lies within a factor 2 of v
+      v[0] = fmaf(-q01[0], up, v[0]);
+      v[1] = fmaf(-q01[1], up, v[1]);
+      v[2] = fmaf(-q23[0], up, v[2]);
+      v[3] = fmaf(-q23[1], up, v[3]);
+      code = (uint32_t)c2;
+    }
+    codes[(slot * 8 + lev) * 32 + dw] = code;
+    scl[(slot * 8 + lev) * 4 + blk] = (uint8_t)e8;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rho = lane & 15, gk = lane >> 4;
+  const int rs = (rho >> 1) & 1, rl = 2 * (rho >> 2) + (rho & 1);
+  const u32x4 lo = *(const u32x4*)(codes + (rs * 8 + rl) * 32 + 8 * gk);
+  const u32x4 hi = *(const u32x4*)(codes + (rs * 8 + rl) * 32 + 8 * gk + 4);
+  LinOp op;
+  op.a = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  op.sc = scl[(rs * 8 + rl) * 4 + gk];
+  return op;
+}
+
+// Four partial head sums: for u = 0..3, the MFMA products of query operand
+// set qa[u] (NHT head tiles) with key tile kt[u], followed by this lane's
+// share of sum_h wq[u][h] * |dot| + (linear term), in the fixed order: the
+// level pair first, then ht = 0..NHT-1, r = 0..3.  u = 2*q + t: query row q
+// of the wave's pair (slot q), key tile t (kt = {t0, t1, t0, t1}); one level
+// MFMA per key tile.
+template <int NHT>
+__device__ __forceinline__ void tile_partials(const v8i* const (&qa)[4], const float (*const (&wq)[4])[4],
+                                              const v8i* const (&kt)[4], const LinOp& lin, float (&acc)[4]) {
+  constexpr int NL = 2;
+  v4f e[NL];
+#pragma unroll
+  for (int t = 0; t < NL; ++t) e[t] = mfma_fp8_16x16x128_sa(lin.a, lin.sc, *kt[t]);
+  v4f d[NHT][4];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[ht][u] = mfma_fp8_16x16x128(qa[u][ht], *kt[u]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const v4f& x = e[u & 1];
+    acc[u] = (u >> 1) ? x[2] + x[3] : x[0] + x[1];
+  }
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[u] = fmaf(wq[u][ht][r], fabsf(d[ht][u][r]), acc[u]);
+  // schedule: pending LDS reads (the next step's operands, if any) first,
+  // then every MFMA back to back, then the epilogue.  With two waves per
+  // SIMD the waves fall into alternation, one streaming MFMAs while the
+  // other runs its VALU epilogue; in a step-body probe this beat any
+  // interleave of MFMA and VALU within a wave by 12-15%.
+  __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NL + 4 * NHT, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 96, 0);
 }
 
 constexpr int kPrefillWaves = 8;
@@ -202,14 +403,18 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   const int k_end = min(k_begin + keys_per_wg, np_last);
   if (k_begin >= k_end) return;
 
+  __shared__ __attribute__((aligned(16))) uint8_t lin_lds[kPrefillWaves * kLinScratch];
+  LinLoads<NHT> ll;
+  lin_load<NHT>(a, b, i0, i0 + 1, lane, ll);
   v8i qa[kRowsPerWave][kMaxHeadTiles];
   float wq[kRowsPerWave][kMaxHeadTiles][4];
 #pragma unroll
   for (int q = 0; q < kRowsPerWave; ++q) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) qa[q][ht] = load_q_tile(a, b, i0 + q, ht, lane);
-    load_weights(a, b, i0 + q, lane, wq[q]);
+    load_weights(a, b, i0 + q, lane, 0.5f, wq[q]);
   }
+  const LinOp lin = lin_operand<NHT>(ll, lane, lin_lds + wave * kLinScratch);
   // After the reduce-scatter, lane group g holds row i0 + g/2, tile g%2.
   const int g = lane >> 4;
   const int my_row = i0 + (g >> 1);
@@ -231,7 +436,7 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
     const v8i n1 = ksr.load(s0 + 48, kl);
     const v8i* kp[4] = {&kt0, &kt1, &kt0, &kt1};
     float p[4];
-    tile_partials<NHT>(qp, wp, kp, p);
+    tile_partials<NHT>(qp, wp, kp, lin, p);
     const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
     if (s < my_np && s < k_end) my_out[s] = tot * ks;
     kt0 = n0;
@@ -313,14 +518,20 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   };
   dma(0, kbuf0, sbuf0);
 
+  LinLoads<NHT> ll;
+  lin_load<NHT>(a, b, i0, i0 + 1, lane, ll);
   v8i qa[kRowsPerWave][kMaxHeadTiles];
   float wq[kRowsPerWave][kMaxHeadTiles][4];
 #pragma unroll
   for (int q = 0; q < kRowsPerWave; ++q) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) qa[q][ht] = load_q_tile(a, b, i0 + q, ht, lane);
-    load_weights(a, b, i0 + q, lane, wq[q]);
+    load_weights(a, b, i0 + q, lane, 0.5f, wq[q]);
   }
+  // The level operand is built in buffer 1, which no DMA writes before the
+  // barrier that publishes sub-block 0.
+  static_assert(kLdsWaves * kLinScratch <= kSubBytes, "level scratch");
+  const LinOp lin = lin_operand<NHT>(ll, lane, kbuf1 + wave * kLinScratch);
   // After the reduce-scatter, lane group g holds row i0 + g/2, key tile g%2.
   const int g = lane >> 4;
   const int kl16 = lane & 15;
@@ -363,7 +574,7 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
     read_step(nk, ns, nsst, nt0, nt1, nks);
     const v8i* kp[4] = {&kt0, &kt1, &kt0, &kt1};
     float p[4];
-    tile_partials<NHT>(qp, wp, kp, p);
+    tile_partials<NHT>(qp, wp, kp, lin, p);
     const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
     const int s = k_begin + 32 * st + 16 * (g & 1) + kl16;
     const int off = s < my_np ? lane_row_off + s * 4 : INT_MAX;
@@ -404,6 +615,9 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
       asm volatile("" ::"v"(qa[q][ht]));
       asm volatile("" ::"v"(wq[q][ht][0]), "v"(wq[q][ht][1]), "v"(wq[q][ht][2]), "v"(wq[q][ht][3]));
     }
+  // ... and the level operand's LDS reads, which must land before buffer 1
+  // is reused
+  asm volatile("" ::"v"(lin.a), "v"(lin.sc));
   wait_dma();
   __syncthreads();   // sub-block 0 staged
   if (nsub > 1) dma(1, kbuf1, sbuf1);
@@ -435,11 +649,8 @@ indexer_decode_kernel(IndexerArgs a) {
   float wq[kMaxHeadTiles][4];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) qa[ht] = load_q_tile(a, b, i, ht, lane);
-  load_weights(a, b, i, lane, wq);
+  load_weights(a, b, i, lane, 1.f, wq);
   float* out = a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld;
-  const v8i* qp[4] = {qa, qa, qa, qa};
-  const float(*wp[4])[4] = {wq, wq, wq, wq};
-
   KeyStream<kFullD> ksr;
   ksr.init(a, b, lane, k_begin);
   const int kl = lane & 15;
@@ -454,7 +665,7 @@ indexer_decode_kernel(IndexerArgs a) {
     for (int u = 0; u < 4; ++u) nx[u] = ksr.load(s0 + 64 + 16 * u, kl);
     const v8i* kp[4] = {&kt[0], &kt[1], &kt[2], &kt[3]};
     float p[4];
-    tile_partials<NHT>(qp, wp, kp, p);
+    tile_partials_relu<NHT>(qa, wq, kp, p);
     const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
     if (s < k_end) out[s] = tot * ks;
 #pragma unroll
@@ -464,6 +675,71 @@ indexer_decode_kernel(IndexerArgs a) {
 
 // The LDS-staged kernel stores through 31-bit byte offsets within two rows.
 bool lds_path_ok(const IndexerArgs& a) { return (2 * a.ld + (int64_t)a.S) * 4 < (int64_t)INT_MAX; }
+
+// Workgroups of the LDS kernel that are resident at once: two per CU.
+int lds_slots() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return 2 * cus[dev];
+}
+
+// Key-block length of the LDS kernel.  A workgroup costs a fixed set-up
+// (q tiles, level operand, first key DMA: about kSetupSteps steps of 32
+// keys, measured) plus one step per 32 keys, and the launch runs in rounds
+// of `slots` workgroups; dispatch takes full key blocks first and each
+// query block's shorter last block at the end.  The length (a multiple of
+// the 256-key sub-block, up to 8192) minimises an estimate of the
+// makespan: whole rounds of full blocks, a last partial round, and the
+// short blocks, which after whole rounds mostly start in the slots freed
+// by the earliest finishers (kAbsorb: the share of their length that
+// still shows).  On 256-row chunks of a 128K prefill this picks the
+// fastest of the lengths measured at every position tried.  The estimate
+// assumes query blocks of about equal extent; spans whose extents differ
+// by 2048 keys or more (a whole causal triangle) return 0, and the caller
+// falls back to its default.  Scores do not depend on it.
+int lds_keys_per_wg(const IndexerArgs& a, int nqb, int slots) {
+  constexpr double kSetupSteps = 13.0, kAbsorb = 0.3;
+  if (!a.pk.seq_lens) {
+    const int64_t np_first = min((int64_t)a.pos0 + min(kLdsRows, a.rows), (int64_t)a.S);
+    const int64_t np_last = min((int64_t)a.pos0 + a.rows, (int64_t)a.S);
+    if (np_last - np_first >= 2048) return 0;
+  }
+  double best_t = 1e300;
+  int best = 2048;
+  for (int kpw = 256; kpw <= 8192; kpw += 256) {
+    int64_t nfull = 0, npart = 0;
+    int dpart = 0;
+    for (int qb = 0; qb < nqb; ++qb) {
+      const int64_t np = a.pk.seq_lens ? a.S : min((int64_t)a.pos0 + min((qb + 1) * kLdsRows, a.rows), (int64_t)a.S);
+      nfull += np / kpw;
+      if (np % kpw) {
+        ++npart;
+        dpart = max(dpart, (int)((np % kpw + 31) / 32));
+      }
+    }
+    nfull *= a.B;
+    npart *= a.B;
+    const double df = kSetupSteps + kpw / 32, dp = kSetupSteps + dpart;
+    const int64_t rounds = nfull / slots, left = nfull % slots, free = slots - left;
+    double t = rounds * df + (left ? df : 0.0);
+    if (npart) {
+      if (left) t += npart <= free ? max(0.0, dp - df) : 0.0;
+      else t += kAbsorb * dp;
+      if (npart > free) t += dp * (double)((npart - free + slots - 1) / slots);
+    }
+    if (t < best_t) {
+      best_t = t;
+      best = kpw;
+    }
+  }
+  return best;
+}
 
 template <int NHT, bool kFullD>
 hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
@@ -477,13 +753,18 @@ hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
   } else {
     const int rows_per_wg = lds_ok ? kLdsRows : kPrefillRows;
     const int nqb = (a.rows + rows_per_wg - 1) / rows_per_wg;
-    // Large key blocks amortise the q loads (8 KB per row); smaller ones
-    // keep at least ~512 workgroups busy.  Results do not depend on it.
-    int keys = 2048;
-    while (keys > 256) {
-      const long long kblocks = (np_max + keys - 1) / keys;
-      if ((long long)nqb * kblocks * a.B >= 512) break;
-      keys >>= 1;
+    // Key-block length: the LDS kernel's makespan estimate where it
+    // applies; otherwise 2048 keys (amortising the q loads, 8 KB per row),
+    // halved while that leaves fewer than ~512 workgroups.  Results do not
+    // depend on it.
+    int keys = lds_ok ? lds_keys_per_wg(a, nqb, lds_slots()) : 0;
+    if (keys == 0) {
+      keys = 2048;
+      while (keys > 256) {
+        const long long kblocks = (np_max + keys - 1) / keys;
+        if ((long long)nqb * kblocks * a.B >= 512) break;
+        keys >>= 1;
+      }
     }
     const int nkb = (np_max + keys - 1) / keys;
     const int nkb8 = (nkb + 7) / 8;
