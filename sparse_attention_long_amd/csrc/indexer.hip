@@ -142,6 +142,20 @@ __device__ __forceinline__ void load_weights(const IndexerArgs& a, int b, int i,
   const int64_t row = (int64_t)b * a.qrows_b + min(i, a.rows - 1);
   const float qs = row_ok ? a.q_scale[row] : 0.f;
   const uint16_t* wr = a.w + row * a.HI;
+  if (a.HI % 4 == 0 && (reinterpret_cast<uintptr_t>(a.w) & 7) == 0) {
+    // the 4 heads of a lane are consecutive: one 8-byte load per head tile
+#pragma unroll
+    for (int ht = 0; ht < kMaxHeadTiles; ++ht) {
+      const int h0 = 16 * ht + 4 * (lane >> 4);
+      const bool ok = row_ok && h0 < a.HI;
+      const uint2 v = *(const uint2*)(wr + min(h0, a.HI - 4));
+      const float w4[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wq[ht][r] = ok ? w4[r] * qs * fold : 0.f;
+    }
+    return;
+  }
 #pragma unroll
   for (int ht = 0; ht < kMaxHeadTiles; ++ht)
 #pragma unroll
@@ -207,60 +221,65 @@ struct LinOp {
   int sc;   // their E8M0 block scale
 };
 
-// Inputs of v for the query rows of the two slots: lane l loads, for heads
-// 8*i + l/8, the 16 code bytes [16*(l%8), +16) and the folded weight.  All
-// loads are issued here at once, ahead of the q tiles, so that their
-// latency overlaps; a slot whose row lies outside [0, rows) loads zeros.
+// Inputs of v for the query rows of the two slots.  Lane l covers the 16
+// code bytes [16*(l%8), +16) of the heads 16*ht + 4*(l/16) + 2*((l/8)%2) + j
+// (ht < NHT, j < 2): heads whose folded weights the lane already holds from
+// load_weights (wq[ht][2*((l/8)%2) + j]).  All loads are issued at once,
+// ahead of the q tiles; a slot whose row lies outside [0, rows) loads zeros.
 template <int NHT>
 struct LinLoads {
   u32x4 x[2][2 * NHT];
-  float wv[2][2 * NHT];
 };
 
 template <int NHT>
 __device__ __forceinline__ void lin_load(const IndexerArgs& a, int b, int r0, int r1, int lane, LinLoads<NHT>& ld) {
-  const int c = lane & 7, e = lane >> 3;   // 16-byte chunk of K, head group
+  const int c = lane & 7;
+  const int hbase = 4 * (lane >> 4) + 2 * ((lane >> 3) & 1);
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     const int i = sl ? r1 : r0;
     const bool row_ok = i >= 0 && i < a.rows;
     const int64_t row = (int64_t)b * a.qrows_b + min(max(i, 0), a.rows - 1);
-    const float qs = row_ok ? a.q_scale[row] : 0.f;
 #pragma unroll
-    for (int i8 = 0; i8 < 2 * NHT; ++i8) {
-      const int h = 8 * i8 + e;
-      const bool ok = row_ok && h < a.HI;
-      const int hc = min(h, a.HI - 1);
-      const float w = bf16_to_f32(a.w[row * a.HI + hc]);
-      ld.wv[sl][i8] = ok ? w * qs * 0.5f : 0.f;
-      ld.x[sl][i8] = load16_or_zero(a.q_idx + (row * a.HI + hc) * a.dI, 16 * c, a.dI, ok);
-    }
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int h = 16 * ht + hbase + j;
+        const bool ok = row_ok && h < a.HI;
+        ld.x[sl][2 * ht + j] = load16_or_zero(a.q_idx + (row * a.HI + min(h, a.HI - 1)) * a.dI, 16 * c, a.dI, ok);
+      }
   }
 }
 
-// v of slot sl, partly reduced.  Lane l first sums its heads 8*i + l/8
-// over 16 values of K, then the sums are combined over lane bits 5 and 4:
-// lane l ends with the sum over the heads j with j % 2 == (l/8) % 2, for
-// k = 16*(l%8) + 4*(l/16) + t, t = 0..3.  Lanes l and l^8 hold the two
-// halves of each total.
+// v of slot sl (weights wq of that row), partly reduced.  Lane l first
+// sums its 2*NHT heads over 16 values of K, then the sums are combined
+// over lane bits 5 and 4: lane l ends with the sum over the heads j with
+// (j/2) % 2 == (l/8) % 2, for k = 16*(l%8) + 4*(l/16) + t, t = 0..3.  Lanes
+// l and l^8 hold the two halves of each total.
 template <int NHT>
-__device__ __forceinline__ void lin_half_sums(const LinLoads<NHT>& ld, int sl, float (&out)[4]) {
+__device__ __forceinline__ void lin_half_sums(const LinLoads<NHT>& ld, int sl, const float (&wq)[kMaxHeadTiles][4],
+                                              int lane, float (&out)[4]) {
+  const bool odd = (lane & 8) != 0;
   float p[16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) p[t] = 0.f;
 #pragma unroll
-  for (int i8 = 0; i8 < 2 * NHT; ++i8) {
-    const float wv = ld.wv[sl][i8];
+  for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-    for (int dw = 0; dw < 4; ++dw) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ld.x[sl][i8][dw], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ld.x[sl][i8][dw], true);
-      p[4 * dw + 0] = fmaf(wv, lo[0], p[4 * dw + 0]);
-      p[4 * dw + 1] = fmaf(wv, lo[1], p[4 * dw + 1]);
-      p[4 * dw + 2] = fmaf(wv, hi[0], p[4 * dw + 2]);
-      p[4 * dw + 3] = fmaf(wv, hi[1], p[4 * dw + 3]);
+    for (int j = 0; j < 2; ++j) {
+      const float w_lo = wq[ht][j], w_hi = wq[ht][2 + j];   // values, not lvalues: keeps wq in registers
+      const float wv = odd ? w_hi : w_lo;
+      const u32x4& x = ld.x[sl][2 * ht + j];
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[dw], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[dw], true);
+        p[4 * dw + 0] = fmaf(wv, lo[0], p[4 * dw + 0]);
+        p[4 * dw + 1] = fmaf(wv, lo[1], p[4 * dw + 1]);
+        p[4 * dw + 2] = fmaf(wv, hi[0], p[4 * dw + 2]);
+        p[4 * dw + 3] = fmaf(wv, hi[1], p[4 * dw + 3]);
+      }
     }
-  }
   // sum over lane bit 5 (p[t] stays in lanes < 32, p[t+8] in lanes >= 32),
   // then over bit 4 (rows 0, 2 keep the first four, rows 1, 3 the last four)
   float r1[8];
@@ -270,14 +289,15 @@ __device__ __forceinline__ void lin_half_sums(const LinLoads<NHT>& ld, int sl, f
   for (int t = 0; t < 4; ++t) out[t] = reduce_rows16(r1[t], r1[t + 4]);
 }
 
-// Level-tile operand from the loads of lin_load (slot 0: row r0, slot 1:
-// row r1).  `scratch` is kLinScratch bytes of LDS owned by this wave
-// (16-byte aligned).
+// Level-tile operand from the loads of lin_load and the rows' folded
+// weights (slot 0: row r0 with wq0, slot 1: row r1 with wq1).  `scratch`
+// is kLinScratch bytes of LDS owned by this wave (16-byte aligned).
 template <int NHT>
-__device__ __forceinline__ LinOp lin_operand(const LinLoads<NHT>& ld, int lane, uint8_t* scratch) {
+__device__ __forceinline__ LinOp lin_operand(const LinLoads<NHT>& ld, const float (&wq0)[kMaxHeadTiles][4],
+                                             const float (&wq1)[kMaxHeadTiles][4], int lane, uint8_t* scratch) {
   float h0[4], h1[4];
-  lin_half_sums<NHT>(ld, 0, h0);
-  lin_half_sums<NHT>(ld, 1, h1);
+  lin_half_sums<NHT>(ld, 0, wq0, lane, h0);
+  lin_half_sums<NHT>(ld, 1, wq1, lane, h1);
   // Sum over lane bit 3, keeping slot 0 in lanes with bit 3 clear and slot
   // 1 in the others: lane l then holds v[slot][16*(l%8) + 4*(l/16) + t].
   const bool odd = (lane & 8) != 0;
@@ -414,7 +434,7 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
     for (int ht = 0; ht < NHT; ++ht) qa[q][ht] = load_q_tile(a, b, i0 + q, ht, lane);
     load_weights(a, b, i0 + q, lane, 0.5f, wq[q]);
   }
-  const LinOp lin = lin_operand<NHT>(ll, lane, lin_lds + wave * kLinScratch);
+  const LinOp lin = lin_operand<NHT>(ll, wq[0], wq[1], lane, lin_lds + wave * kLinScratch);
   // After the reduce-scatter, lane group g holds row i0 + g/2, tile g%2.
   const int g = lane >> 4;
   const int my_row = i0 + (g >> 1);
@@ -531,7 +551,7 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   // The level operand is built in buffer 1, which no DMA writes before the
   // barrier that publishes sub-block 0.
   static_assert(kLdsWaves * kLinScratch <= kSubBytes, "level scratch");
-  const LinOp lin = lin_operand<NHT>(ll, lane, kbuf1 + wave * kLinScratch);
+  const LinOp lin = lin_operand<NHT>(ll, wq[0], wq[1], lane, kbuf1 + wave * kLinScratch);
   // After the reduce-scatter, lane group g holds row i0 + g/2, key tile g%2.
   const int g = lane >> 4;
   const int kl16 = lane & 15;
