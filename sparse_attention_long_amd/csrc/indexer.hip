@@ -394,25 +394,69 @@ __device__ __forceinline__ void tile_partials(const v8i* const (&qa)[4], const f
   __builtin_amdgcn_sched_group_barrier(0x002, 96, 0);
 }
 
+// Workgroup -> (query block, key block).  Dispatch places workgroup id on
+// XCD id % 8, and the workgroups of one XCD share that XCD's L2.
+//   mode 0: XCD x takes the key blocks kb = 8j + x, query block fastest, so
+//           a key block is read into one L2 only; balanced when the key
+//           block count is a multiple of 8.
+//   mode 1: XCD x takes the tiles [x*per, (x+1)*per) of the order
+//           t = kb*nqb + qb: balanced counts, and an XCD still walks the
+//           query blocks of one or two key blocks.
+//   mode 2: XCD x takes the query blocks qb = 8j + x of every key block
+//           (per = query blocks per XCD): balanced even when the query
+//           blocks' extents differ, at the cost of every L2 reading every
+//           key block.
+struct TileMap {
+  int nqb, nkb, mode, per;
+};
+
+__device__ __forceinline__ bool tile_of(const TileMap& m, int id, int& qb, int& kb) {
+  const int xcd = id & 7, j = id >> 3;
+  if (m.mode == 0) {
+    qb = j % m.nqb;
+    kb = (j / m.nqb) * 8 + xcd;
+    return kb < m.nkb;
+  }
+  if (m.mode == 1) {
+    const int t = xcd * m.per + j;
+    if (j >= m.per || t >= m.nqb * m.nkb) return false;
+    kb = t / m.nqb;
+    qb = t % m.nqb;
+    return true;
+  }
+  qb = (j % m.per) * 8 + xcd;
+  kb = j / m.per;
+  return qb < m.nqb && kb < m.nkb;
+}
+
+unsigned grid_of(const TileMap& m) {
+  if (m.mode == 0) return (unsigned)(8 * m.nqb * ((m.nkb + 7) / 8));
+  if (m.mode == 1) return (unsigned)(8 * m.per);
+  return (unsigned)(8 * m.per * m.nkb);
+}
+
+TileMap make_tile_map(int nqb, int nkb, int mode) {
+  TileMap m{nqb, nkb, mode, 0};
+  if (mode == 1) m.per = (int)(((int64_t)nqb * nkb + 7) / 8);
+  if (mode == 2) m.per = (nqb + 7) / 8;
+  return m;
+}
+
 constexpr int kPrefillWaves = 8;
 constexpr int kRowsPerWave = 2;
 constexpr int kPrefillRows = kPrefillWaves * kRowsPerWave;   // 16 query rows per workgroup
 
 // Work tile = (16 query rows, keys_per_wg keys) of one sequence; each wave
 // owns 2 rows and consumes two 16-key tiles per step (the four partials of
-// a step are (row, tile) pairs).  Tiles are numbered so that the workgroups
-// of one XCD (dispatch goes round-robin over the 8 XCDs) share key blocks:
-// tile id -> xcd = id % 8, then q-block fastest within the XCD, and the
-// XCD's key blocks are kb = 8 * j + xcd.
+// a step are (row, tile) pairs).  Workgroups map to tiles through `map`
+// (TileMap: key blocks or query blocks spread over the 8 XCDs).
 template <int NHT, bool kFullD>
 __global__ void __launch_bounds__(kPrefillWaves * kWave)
-indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
+indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, TileMap map) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int id = blockIdx.x;
-  const int xcd = id & 7, jx = id >> 3;
-  const int qb = jx % nqb;
-  const int kb = (jx / nqb) * 8 + xcd;
+  int qb, kb;
+  if (!tile_of(map, blockIdx.x, qb, kb)) return;   // block-uniform
   const int b = blockIdx.y;
   const int i0 = qb * kPrefillRows + wave * kRowsPerWave;
   if (i0 >= a.rows) return;
@@ -489,7 +533,7 @@ constexpr int kLdsRows = kLdsWaves * kRowsPerWave;   // 8 query rows per workgro
 // keeps the MFMA results in VGPRs where the epilogue reads them directly.
 template <int NHT, int NW>
 __global__ void __launch_bounds__(NW * kWave, 2)
-indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
+indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, TileMap map) {
   constexpr int kRows = NW * kRowsPerWave;
   static_assert(32 % NW == 0 && NW >= 4, "DMA split");
   // Two separate arrays (not one indexed array), so that the compiler can
@@ -500,10 +544,8 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, int nqb) {
   __shared__ __attribute__((aligned(16))) float sbuf1[kSubKeys];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps the store descriptor scalar
-  const int id = blockIdx.x;
-  const int xcd = id & 7, jx = id >> 3;
-  const int qb = jx % nqb;
-  const int kb = (jx / nqb) * 8 + xcd;
+  int qb, kb;
+  if (!tile_of(map, blockIdx.x, qb, kb)) return;   // block-uniform
   const int b = blockIdx.y;
   const int i0 = qb * kRows + wave * kRowsPerWave;
   // Block-uniform extent: every wave takes part in the DMA and barriers.
@@ -761,6 +803,22 @@ int lds_keys_per_wg(const IndexerArgs& a, int nqb, int slots) {
   return best;
 }
 
+// Tile-to-XCD mapping of a prefill launch (see TileMap).  Mode 0 keeps each
+// key block in one L2, but with fewer than 8 key blocks it leaves XCDs
+// without work, and with query blocks of unequal extent (a causal triangle)
+// the XCDs that hold the high key blocks idle.  Mode 2 is balanced in both
+// cases: a 4096-row triangle took 95 us with it against 372 us with mode 0,
+// while on 256-row chunks of a 128K prefill the two were within noise.
+int tile_map_mode(const IndexerArgs& a, int rows_per_wg, int nkb) {
+  if (nkb < 8) return 2;
+  if (!a.pk.seq_lens) {
+    const int64_t np_first = min((int64_t)a.pos0 + min(rows_per_wg, a.rows), (int64_t)a.S);
+    const int64_t np_last = min((int64_t)a.pos0 + a.rows, (int64_t)a.S);
+    if (np_last - np_first >= 2048) return 2;
+  }
+  return 0;
+}
+
 template <int NHT, bool kFullD>
 hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
   // longest row (with per-sequence lengths the host only knows the bound S)
@@ -787,12 +845,12 @@ hipError_t launch_nht(const IndexerArgs& a, bool decode_form, hipStream_t st) {
       }
     }
     const int nkb = (np_max + keys - 1) / keys;
-    const int nkb8 = (nkb + 7) / 8;
-    dim3 grid((unsigned)(8 * nqb * nkb8), a.B);
+    const TileMap map = make_tile_map(nqb, nkb, tile_map_mode(a, rows_per_wg, nkb));
+    dim3 grid(grid_of(map), a.B);
     if (lds_ok)
-      hipLaunchKernelGGL((indexer_prefill_lds_kernel<NHT, kLdsWaves>), grid, dim3(kLdsWaves * kWave), 0, st, a, keys, nqb);
+      hipLaunchKernelGGL((indexer_prefill_lds_kernel<NHT, kLdsWaves>), grid, dim3(kLdsWaves * kWave), 0, st, a, keys, map);
     else
-      hipLaunchKernelGGL((indexer_prefill_kernel<NHT, kFullD>), grid, dim3(kPrefillWaves * kWave), 0, st, a, keys, nqb);
+      hipLaunchKernelGGL((indexer_prefill_kernel<NHT, kFullD>), grid, dim3(kPrefillWaves * kWave), 0, st, a, keys, map);
   }
   return hipGetLastError();
 }
