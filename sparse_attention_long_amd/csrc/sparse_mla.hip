@@ -323,8 +323,20 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int rowid = blockIdx.x / a.nsplit;       // b * rows + i
-  const int sp = blockIdx.x % a.nsplit;
+  // Workgroup -> (row b * rows + i, split).  Dispatch places workgroup id
+  // on XCD id % 8; the splits of a row read the same Q (147 KB for 128
+  // heads) and their partials are combined together, so they go to one
+  // XCD: XCD x takes rows 8j + x, a row's splits consecutively.
+  int rowid, sp;
+  if (a.nsplit == 1) {
+    rowid = blockIdx.x;
+    sp = 0;
+  } else {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    sp = j % a.nsplit;
+    rowid = (j / a.nsplit) * 8 + xcd;
+    if (rowid >= a.B * a.rows) return;   // block-uniform, before any barrier
+  }
   const int b = rowid / a.rows;
   const int i = rowid % a.rows;
   const int64_t qrow = (int64_t)b * a.qrows_b + i;
@@ -694,8 +706,11 @@ __global__ void __launch_bounds__(NW * kWave, 1) indexer_kl_kernel(KlArgs ka) {
 // Merge split partials: lse = log sum_j exp(lse_j), o = sum_j exp(lse_j - lse) o_j.
 template <int DV>
 __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
-  const int rowid = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
+  // (row, head) on the XCD that ran the row's splits (rows 8j + x on XCD x)
+  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+  const int rowid = (jw / a.H) * 8 + xcd;
+  const int h = jw % a.H;
+  if (rowid >= a.B * a.rows) return;
   const int b = rowid / a.rows, i = rowid % a.rows;
   const int64_t qrow = (int64_t)b * a.qrows_b + i;
   const float* pl = a.part_lse + (int64_t)rowid * a.nsplit * a.H + h;
@@ -728,14 +743,15 @@ __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
 
 template <int DK, int DV, int NW>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)(a.B * a.rows * a.nsplit);
+  const int nrow = a.B * a.rows, nrow8 = (nrow + 7) / 8;
+  const unsigned grid = a.nsplit == 1 ? (unsigned)nrow : (unsigned)(8 * nrow8 * a.nsplit);
   if (a.pk.page_table)
     hipLaunchKernelGGL((sparse_mla_kernel<DK, DV, NW, true>), dim3(grid), dim3(NW * kWave), 0, st, a);
   else
     hipLaunchKernelGGL((sparse_mla_kernel<DK, DV, NW, false>), dim3(grid), dim3(NW * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3((unsigned)(a.B * a.rows * a.H)), dim3(DV / 4), 0, st, a);
+  hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3((unsigned)(8 * nrow8 * a.H)), dim3(DV / 4), 0, st, a);
   return hipGetLastError();
 }
 
