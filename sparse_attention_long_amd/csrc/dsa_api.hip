@@ -138,7 +138,8 @@ int64_t forward_chunk_rows(const dsa_dims* d) {
 
 struct ForwardLayout {
   int64_t tc;
-  size_t scores_off, idx_off, part_off, total;
+  int topk_parts;   // top-k workgroups per row (1: one per row)
+  size_t scores_off, idx_off, part_off, topk_off, total;
 };
 
 ForwardLayout forward_layout(const dsa_dims* d) {
@@ -148,7 +149,9 @@ ForwardLayout forward_layout(const dsa_dims* d) {
   L.scores_off = 0;
   L.idx_off = up((size_t)d->batch * L.tc * d->n_kv * sizeof(float));
   L.part_off = L.idx_off + up((size_t)d->batch * L.tc * d->topk * sizeof(int32_t));
-  L.total = L.part_off + up(attn_partial_bytes(d, L.tc));
+  L.topk_off = L.part_off + up(attn_partial_bytes(d, L.tc));
+  L.topk_parts = dsa::topk_split_parts((int64_t)d->batch * L.tc, d->n_kv);
+  L.total = L.topk_off + up(dsa::topk_split_bytes((int64_t)d->batch * L.tc, L.topk_parts));
   return L;
 }
 
@@ -338,7 +341,7 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     ta.pos0 = pos_base + (int)i0;
     ta.S = d->n_kv;
     ta.k = d->topk;
-    e = dsa::launch_topk(ta, s);
+    e = dsa::launch_topk_split(ta, L.topk_parts, wsb + L.topk_off, s);
     if (e != hipSuccess) return hip_status(e, "top-k launch");
 
     dsa::AttnArgs aa{};

@@ -87,6 +87,13 @@ constexpr int kIndexerDecodeMaxRows = 4;
 
 hipError_t launch_indexer(const IndexerArgs& a, bool decode_form, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// Split top-k for few long rows: each row's collection is spread over
+// nparts workgroups whose candidates meet in a caller workspace of
+// topk_split_bytes(rows_total, nparts) bytes; the selection is the same as
+// launch_topk's.  nparts <= 1 runs launch_topk.
+int topk_split_parts(int64_t rows_total, int S);
+size_t topk_split_bytes(int64_t rows_total, int nparts);
+hipError_t launch_topk_split(const TopkArgs& a, int nparts, void* ws, hipStream_t st);
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st);
 // Indexer KL of each row over its selection: `at` as for the attention, with
 // at.lse the attention's log-sum-exp (input), at.out unused.

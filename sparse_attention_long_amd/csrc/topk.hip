@@ -185,7 +185,139 @@ __device__ __forceinline__ void scan_row(const RowSplit& r, F&& f, G&& g) {
   if (t >= 4 && t - 4 < r.n - r.tail0) g(r.tail0 + t - 4, order_key(r.x[r.tail0 + t - 4]));
 }
 
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
+// Candidates of a row collected by the parts of topk_collect_kernel.
+struct Parts {
+  uint32_t* cnt;   // [rows_total * nparts] keys each part found at or above its cutoff
+  uint32_t* key;   // [rows_total * nparts * kCapPart]
+  uint32_t* idx;
+  int nparts;
+};
+constexpr int kCapPart = 4096;   // candidates kept per part
+
+// Sampled cutoff of a row: 32 blocks of 64 scores spread over the row give
+// a conservative lower bound lo for tau (the sample's rank-r 13-bit bin, r
+// chosen so that about 2m keys are expected at or above it).  hist (kBins1,
+// zero on entry) is zero again on return.
+__device__ __forceinline__ uint32_t sampled_cutoff(const RowSplit& row, int n, int m, uint32_t* hist, Shared& sh) {
+  const int t = threadIdx.x;
+  const int blk = t >> 5;
+  const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + 2 * (t & 31);
+  atomicAdd(&hist[order_key(row.x[e0]) >> kShift1], 1u);
+  atomicAdd(&hist[order_key(row.x[e0 + 1]) >> kShift1], 1u);
+  __syncthreads();
+  const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
+  find_bin(hist, kBins1, r, sh);
+  const uint32_t lo = sh.bin << kShift1;
+  for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
+  return lo;
+}
+
+// Appends every key >= lo of the row's vector elements [q0, q1) (float4
+// units), plus the scalar head (head) and tail (tail) elements, with its
+// index, to the LDS candidate list (sh.ncand counts all of them, also past
+// cap).  One wave-level append per iteration: each lane marks its
+// candidates among its 4 x 4 scores, the wave forms the prefix of the
+// counts from ballots, and one LDS atomic reserves the wave's slots.
+__device__ __forceinline__ void collect_range(const RowSplit& row, int q0, int q1, bool head, bool tail_part,
+                                              uint32_t lo, uint32_t* ckey, uint32_t* cidx, int cap, Shared& sh) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int iters = (q1 - q0 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  for (int it = 0; it < iters; ++it) {
+    float4 v[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = q0 + (it * kUnroll + u) * kThreads + t;
+      ok[u] = q < q1;
+      v[u] = row.xv[ok[u] ? q : 0];
+    }
+    uint32_t keys[4 * kUnroll];
+    uint32_t cm = 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      keys[4 * u + 0] = order_key(v[u].x);
+      keys[4 * u + 1] = order_key(v[u].y);
+      keys[4 * u + 2] = order_key(v[u].z);
+      keys[4 * u + 3] = order_key(v[u].w);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cm |= (ok[u] && keys[4 * u + c] >= lo ? 1u : 0u) << (4 * u + c);
+    }
+    uint32_t total;
+    const uint32_t pre = wave_prefix_small((uint32_t)__popc(cm), total);
+    if (total != 0) {   // wave-uniform
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sh.ncand, total);
+      base = __shfl(base, 0, 64);
+      uint32_t pos = base + pre;
+#pragma unroll
+      for (int j = 0; j < 4 * kUnroll; ++j) {
+        if ((cm >> j) & 1u) {
+          if (pos < (uint32_t)cap) {
+            ckey[pos] = keys[j];
+            cidx[pos] = (uint32_t)(row.h + 4 * (q0 + (it * kUnroll + (j >> 2)) * kThreads + t) + (j & 3));
+          }
+          ++pos;
+        }
+      }
+    }
+  }
+  auto one = [&](int e) {
+    const uint32_t key = order_key(row.x[e]);
+    if (key >= lo) {
+      const uint32_t pos = atomicAdd(&sh.ncand, 1u);
+      if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
+    }
+  };
+  if (head && t < row.h) one(t);
+  if (tail_part && t >= 4 && t - 4 < row.n - row.tail0) one(row.tail0 + t - 4);
+}
+
+// Collection half of the split top-k: part f of a row (nparts per row, row
+// b * rows + i = blockIdx.x / nparts) takes the row's sampled cutoff (every
+// part computes the same one) and collects the keys at or above it among
+// its share of the row into the workspace.  Short rows (n <= k) write a
+// zero count; the merge kernel handles them.
+__global__ void __launch_bounds__(kThreads) topk_collect_kernel(TopkArgs a, Parts parts) {
+  extern __shared__ uint32_t lds[];
+  __shared__ Shared sh;
+  const int t = threadIdx.x;
+  const int f = blockIdx.x % parts.nparts;
+  const int rowid = blockIdx.x / parts.nparts;
+  const int b = rowid / a.rows, i = rowid % a.rows;
+  const int n = min(row_pos_base(a.pk, b, a.S, a.pos0) + i + 1, a.S);
+  const int m = min(a.k, n);
+  uint32_t* cnt = parts.cnt + (int64_t)rowid * parts.nparts + f;
+  if (n <= a.k) {
+    if (t == 0) *cnt = 0u;
+    return;
+  }
+  const RowSplit row(a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld, n);
+  uint32_t* hist = lds;
+  uint32_t* ckey = hist + kBins1;
+  uint32_t* cidx = ckey + kCapPart;
+  for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
+  if (t == 0) sh.ncand = 0;
+  __syncthreads();
+  const uint32_t lo = sampled_cutoff(row, n, m, hist, sh);
+  const int q0 = (int)((int64_t)row.nq * f / parts.nparts), q1 = (int)((int64_t)row.nq * (f + 1) / parts.nparts);
+  collect_range(row, q0, q1, f == 0, f == parts.nparts - 1, lo, ckey, cidx, kCapPart, sh);
+  __syncthreads();
+  const uint32_t nc = sh.ncand;
+  const int64_t base = ((int64_t)rowid * parts.nparts + f) * kCapPart;
+  for (int j = t; j < (int)min(nc, (uint32_t)kCapPart); j += kThreads) {
+    parts.key[base + j] = ckey[j];
+    parts.idx[base + j] = cidx[j];
+  }
+  if (t == 0) *cnt = nc;
+}
+
+// The selection of one row (blockIdx.x = b * rows + i).  kParts: the
+// candidates come from topk_collect_kernel's parts when they are usable
+// (no part overflowed and m <= total <= cap), else the row takes the
+// two-pass fallback; otherwise the row is sampled and collected here.
+template <bool kParts>
+__device__ __forceinline__ void topk_row(const TopkArgs& a, int cap, const Parts& parts) {
   extern __shared__ uint32_t lds[];
   __shared__ Shared sh;
   const int t = threadIdx.x;
@@ -240,78 +372,38 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
     }
   };
 
-  // ---- one pass with a sampled cutoff: 32 blocks of 64 scores spread over
-  // the row give a conservative lower bound lo for tau (the sample's rank-r
-  // bin, r chosen so that about 2m keys are expected at or above it); the
-  // row is then read once and every key >= lo is collected.  If between m
-  // and cap keys were collected, tau is the m-th largest candidate and the
-  // selection is exact; otherwise the two-pass radix select below runs.
+  // ---- one pass with a sampled cutoff (or the parts' candidates): if
+  // between m and cap keys were collected, tau is the m-th largest candidate
+  // and the selection is exact; otherwise the two-pass radix select below
+  // runs.
   bool done = false;
   {
-    const int blk = t >> 5;
-    const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + 2 * (t & 31);
-    atomicAdd(&hist[order_key(row.x[e0]) >> kShift1], 1u);
-    atomicAdd(&hist[order_key(row.x[e0 + 1]) >> kShift1], 1u);
-    __syncthreads();
-    const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
-    find_bin(hist, kBins1, r, sh);
-    const uint32_t lo = sh.bin << kShift1;
-    for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
-    {
-      // One wave-level append per iteration: each lane marks its candidates
-      // among its 4 x 4 scores, the wave forms the prefix of the counts from
-      // ballots, and one LDS atomic reserves the wave's slots.
-      const int lane = t & 63;
-      const int iters = (row.nq + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-      for (int it = 0; it < iters; ++it) {
-        float4 v[kUnroll];
-        bool ok[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int q = (it * kUnroll + u) * kThreads + t;
-          ok[u] = q < row.nq;
-          v[u] = row.xv[ok[u] ? q : 0];
-        }
-        uint32_t keys[4 * kUnroll];
-        uint32_t cm = 0;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          keys[4 * u + 0] = order_key(v[u].x);
-          keys[4 * u + 1] = order_key(v[u].y);
-          keys[4 * u + 2] = order_key(v[u].z);
-          keys[4 * u + 3] = order_key(v[u].w);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) cm |= (ok[u] && keys[4 * u + c] >= lo ? 1u : 0u) << (4 * u + c);
-        }
-        uint32_t total;
-        const uint32_t pre = wave_prefix_small((uint32_t)__popc(cm), total);
-        if (total != 0) {   // wave-uniform
-          const int leader = 0;
-          uint32_t base = 0;
-          if (lane == leader) base = atomicAdd(&sh.ncand, total);
-          base = __shfl(base, leader, 64);
-          uint32_t pos = base + pre;
-#pragma unroll
-          for (int j = 0; j < 4 * kUnroll; ++j) {
-            if ((cm >> j) & 1u) {
-              if (pos < (uint32_t)cap) {
-                ckey[pos] = keys[j];
-                cidx[pos] = (uint32_t)(row.h + 4 * ((it * kUnroll + (j >> 2)) * kThreads + t) + (j & 3));
-              }
-              ++pos;
-            }
+    if constexpr (kParts) {
+      const int64_t pr = (int64_t)blockIdx.x * parts.nparts;
+      uint32_t tot = 0;
+      bool over = false;
+      for (int f = 0; f < parts.nparts; ++f) {
+        const uint32_t c = parts.cnt[pr + f];
+        tot += c;
+        over = over || c > (uint32_t)kCapPart;
+      }
+      const bool use = !over && tot >= (uint32_t)m && tot <= (uint32_t)cap;   // block-uniform
+      if (use) {
+        uint32_t off = 0;
+        for (int f = 0; f < parts.nparts; ++f) {
+          const uint32_t c = parts.cnt[pr + f];
+          const int64_t base = (pr + f) * kCapPart;
+          for (int j = t; j < (int)c; j += kThreads) {
+            ckey[off + j] = parts.key[base + j];
+            cidx[off + j] = parts.idx[base + j];
           }
+          off += c;
         }
       }
-      auto tail = [&](int e) {
-        const uint32_t key = order_key(row.x[e]);
-        if (key >= lo) {
-          const uint32_t pos = atomicAdd(&sh.ncand, 1u);
-          if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
-        }
-      };
-      if (t < row.h) tail(t);
-      if (t >= 4 && t - 4 < row.n - row.tail0) tail(row.tail0 + t - 4);
+      if (t == 0) sh.ncand = use ? tot : (uint32_t)cap + 1u;
+    } else {
+      const uint32_t lo = sampled_cutoff(row, n, m, hist, sh);
+      collect_range(row, 0, row.nq, true, true, lo, ckey, cidx, cap, sh);
     }
     __syncthreads();
     const uint32_t nc = sh.ncand;
@@ -421,26 +513,82 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) {
   for (int j = m + t; j < a.k; j += kThreads) out[j] = -1;
 }
 
+__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) { topk_row<false>(a, cap, Parts{}); }
+
+__global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a, int cap, Parts parts) {
+  topk_row<true>(a, cap, parts);
+}
+
+// Candidate capacity of the single-row selection: what the LDS budget
+// leaves, at most kMaxCand (at the largest supported S this is still ~7900,
+// above any plausible cutoff bin).
+int row_cap(const TopkArgs& a, size_t& lds) {
+  const size_t words = (size_t)((a.S + 31) >> 5);
+  const size_t fixed = (kBins1 + 2 * words) * sizeof(uint32_t);
+  const int cap = (int)min((size_t)kMaxCand, (kDynLds - fixed) / (2 * sizeof(uint32_t)));
+  lds = fixed + 2 * (size_t)cap * sizeof(uint32_t);
+  return cap;
+}
+
+hipError_t set_dyn_lds(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+}
+
 }  // namespace
 
 int topk_max_kv() { return kMaxKV; }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.rows <= 0 || a.B <= 0) return hipSuccess;
-  const size_t words = (size_t)((a.S + 31) >> 5);
-  const size_t fixed = (kBins1 + 2 * words) * sizeof(uint32_t);
-  // Candidate capacity: what the LDS budget leaves, at most kMaxCand (at the
-  // largest supported S this is still ~7900, above any plausible cutoff bin).
-  const int cap = (int)min((size_t)kMaxCand, (kDynLds - fixed) / (2 * sizeof(uint32_t)));
-  const size_t lds = fixed + 2 * (size_t)cap * sizeof(uint32_t);
+  size_t lds = 0;
+  const int cap = row_cap(a, lds);
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+    const hipError_t e = set_dyn_lds((const void*)topk_kernel);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a, cap);
+  return hipGetLastError();
+}
+
+int topk_split_parts(int64_t rows_total, int S) {
+  // Few long rows leave most CUs idle with one workgroup per row: spread
+  // each row's collection over up to 8 workgroups (about 256 in all).
+  if (S < 16384 || rows_total <= 0 || rows_total > 128) return 1;
+  const int64_t p = 256 / rows_total;
+  return (int)(p < 2 ? 2 : p > 8 ? 8 : p);
+}
+
+size_t topk_split_bytes(int64_t rows_total, int nparts) {
+  if (nparts <= 1) return 0;
+  const size_t n = (size_t)rows_total * nparts;
+  return (n * sizeof(uint32_t) + 255) / 256 * 256 + 2 * n * kCapPart * sizeof(uint32_t);
+}
+
+hipError_t launch_topk_split(const TopkArgs& a, int nparts, void* ws, hipStream_t st) {
+  if (a.rows <= 0 || a.B <= 0) return hipSuccess;
+  if (nparts <= 1) return launch_topk(a, st);
+  const size_t n = (size_t)a.B * a.rows * nparts;
+  Parts parts;
+  parts.cnt = (uint32_t*)ws;
+  parts.key = (uint32_t*)((char*)ws + (n * sizeof(uint32_t) + 255) / 256 * 256);
+  parts.idx = parts.key + n * kCapPart;
+  parts.nparts = nparts;
+  size_t lds = 0;
+  const int cap = row_cap(a, lds);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = set_dyn_lds((const void*)topk_collect_kernel);
+    if (e == hipSuccess) e = set_dyn_lds((const void*)topk_merge_kernel);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t lds_collect = (kBins1 + 2 * (size_t)kCapPart) * sizeof(uint32_t);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)n), dim3(kThreads), lds_collect, st, a, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a, cap, parts);
   return hipGetLastError();
 }
 

@@ -98,6 +98,10 @@ INDEXER_CASES = {
     "decode_b3": W.custom("dec64", batch=3, n_kv=5003, q_pos0=5002),
     "decode_t3": W.custom("dec64", batch=2, n_q=3, n_kv=4099, q_pos0=4096),
     "two_chunks": W.custom("p4k", n_q=1024, n_kv=65536, q_pos0=64512),
+    # few long decode rows: the fused forward spreads each row's top-k over
+    # several workgroups (odd length: ragged vector split and scalar tail)
+    "decode_long_b4": W.custom("dec64", batch=4, n_kv=20011, q_pos0=20010),
+    "decode_long_t3": W.custom("dec64", batch=2, n_q=3, n_kv=33000, q_pos0=32997),
 }
 
 
@@ -287,7 +291,8 @@ def run_forward(wl, d, with_idx=True):
     return out, lse, idx
 
 
-@pytest.mark.parametrize("name", ["tiny", "p4k", "decode_b3", "chunk_pos0", "two_chunks"])
+@pytest.mark.parametrize("name", ["tiny", "p4k", "decode_b3", "chunk_pos0", "two_chunks", "decode_long_b4",
+                                  "decode_long_t3"])
 def test_forward_bitwise_equals_chained_calls(name):
     wl = W.WORKLOADS.get(name) or INDEXER_CASES[name]
     d = SD.fill_inputs(wl)
