@@ -124,7 +124,9 @@ int dsa_sparse_mla_attn(const dsa_dims* dims, const uint16_t* q, const uint16_t*
 /*
  * The whole forward path: indexer -> top-k -> sparse MLA, processed in
  * chunks of query rows so that each chunk's scores stay in a workspace
- * slice.  Inputs and outputs are those of the three calls above.
+ * slice (the workspace also holds the selection, the attention's split
+ * partials and, for a few long rows, the top-k's per-part candidate lists).
+ * Inputs and outputs are those of the three calls above.
  *   idx_out  [B, T, topk] int32 or NULL: if given, receives the selection.
  * The result equals, bit for bit, running dsa_indexer_scores, dsa_topk and
  * dsa_sparse_mla_attn one after the other.
