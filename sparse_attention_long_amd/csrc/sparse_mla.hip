@@ -162,10 +162,12 @@ struct RowGather {
     const int r = q / C::kPB, pp = q % C::kPB;
     off_b = (uint64_t)max(rb, 0) * (uint64_t)(DK * 2) + 16u * (uint32_t)(C::kPA + (pp ^ (r & (C::kPB - 1))));
   }
-  __device__ __forceinline__ void issue_all(uint16_t* tile, const uint16_t* kvb, int wave) const {
+  static constexpr int kPerWave = C::kDmaA / NW + 1;   // copy instructions per wave and chunk
+  // Copy instruction jj (< kPerWave) of this wave: part-A row jj * NW + wave,
+  // or (jj = kPerWave - 1) the wave's part-B block.
+  __device__ __forceinline__ void issue(int jj, uint16_t* tile, const uint16_t* kvb, int wave) const {
     const uint32_t t0 = lds_addr(tile);
-#pragma unroll
-    for (int jj = 0; jj < C::kDmaA / NW; ++jj) {
+    if (jj < C::kDmaA / NW) {
       const int j = jj * NW + wave;
       const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)off_a, j);
       if constexpr (K64) {
@@ -175,12 +177,38 @@ struct RowGather {
       } else {
         dma_x4_s((lane16 ^ (16u * (uint32_t)(jj & 3))) + lo, kvb, t0 + (uint32_t)j * (C::kRA * 16));
       }
-    }
-    if constexpr (K64)
+    } else if constexpr (K64) {
       dma_x4((const uint8_t*)kvb + off_b, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
-    else
+    } else {
       dma_x4_s((uint32_t)off_b, kvb, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
+    }
   }
+  __device__ __forceinline__ void issue_all(uint16_t* tile, const uint16_t* kvb, int wave) const {
+#pragma unroll
+    for (int jj = 0; jj < kPerWave; ++jj) issue(jj, tile, kvb, wave);
+  }
+};
+
+// A wave's copies of one later chunk, issued one at a time between MFMAs
+// (issue(jj) does nothing when `more` is false).  Used where registers
+// allow it: in the attention kernel the held state made the allocator
+// spill the O^T accumulator.
+template <int DK, int DV, int NW, bool K64>
+struct LaterCopies {
+  RowGather<DK, DV, NW, K64> g;
+  uint16_t* tile;
+  const uint16_t* kvb;
+  int wave;
+  bool more;
+  static constexpr int kPerWave = RowGather<DK, DV, NW, K64>::kPerWave;
+  __device__ __forceinline__ void issue(int jj) const {
+    if (more) g.issue(jj, tile, kvb, wave);
+  }
+};
+
+struct NoCopies {
+  static constexpr int kPerWave = 0;
+  __device__ __forceinline__ void issue(int) const {}
 };
 
 template <int N>
@@ -497,8 +525,11 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
 // plus one half swap.  The four waves' sums meet in a two-chunk LDS ring
 // that each wave folds (8 keys each) one chunk later; the tile barrier
 // orders the accesses.
-template <int DK, int DV, int NW>
-__device__ __forceinline__ v16f qk_chunk_heads(const uint16_t* tb, const v8bf (&qb)[DK / 16]) {
+// `cp.issue(jj)` issues this wave's copy instruction jj (of CP::kPerWave)
+// for a later chunk, spread evenly over the K steps so that the memory
+// pipeline drains the copies while the matrix core works.
+template <int DK, int DV, int NW, typename CP>
+__device__ __forceinline__ v16f qk_chunk_heads(const uint16_t* tb, const v8bf (&qb)[DK / 16], const CP& cp) {
   using C = Cfg<DK, DV, NW>;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -521,6 +552,9 @@ __device__ __forceinline__ v16f qk_chunk_heads(const uint16_t* tb, const v8bf (&
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(qb[ks]), "v"(cur));
     else
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(st) : "v"(qb[ks]), "v"(cur));
+#pragma unroll
+    for (int jj = 0; jj < CP::kPerWave; ++jj)
+      if (jj * C::kKS / CP::kPerWave == ks) cp.issue(jj);
   }
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(st));
   return st;
@@ -658,10 +692,23 @@ __global__ void __launch_bounds__(NW * kWave, 1) indexer_kl_kernel(KlArgs ka) {
     if (c + 1 < nchunks) wait_vm<ndma>(); else wait_vm<0>();
     // the LDS head sums of chunk c-1 must have landed before wave 0 reads them
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 2 < nchunks) gather(fill, ra, rb);
-    if (c > 0) fold(c - 1);
+    v16f st;
+    if constexpr (C::kRowDma) {
+      // chunk c+2's copies ride along this chunk's QK steps
+      LaterCopies<DK, DV, NW, kPaged> cp;
+      cp.g.init(ra, rb, wv);
+      cp.tile = fill;
+      cp.kvb = kvb;
+      cp.wave = wv;
+      cp.more = c + 2 < nchunks;
+      if (c > 0) fold(c - 1);
+      st = qk_chunk_heads<DK, DV, NW>(cur, qb, cp);
+    } else {
+      if (c + 2 < nchunks) gather(fill, ra, rb);
+      if (c > 0) fold(c - 1);
+      st = qk_chunk_heads<DK, DV, NW>(cur, qb, NoCopies{});
+    }
     const bool kval = rv >= 0;   // this lane's key (col) is a selected entry
-    const v16f st = qk_chunk_heads<DK, DV, NW>(cur, qb);
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) ps += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j], zscale, -lse2[j]));
