@@ -520,9 +520,10 @@ indexer_prefill_kernel(IndexerArgs a, int keys_per_wg, TileMap map) {
 //
 // The B operands of step st+1 are read from LDS while step st's MFMAs run
 // (two register sets alternate with the step parity).  The per-score
-// arithmetic is tile_partials', as in every other indexer path.  NW = 4
-// waves per workgroup lets two workgroups share a CU, so one's barrier
-// waits and prologue are covered by the other's work.
+// arithmetic is tile_partials', as in the register-streaming prefill
+// kernel.  NW = 4 waves per workgroup lets two workgroups share a CU, so
+// one's barrier waits and prologue are covered by the other's work, and
+// the two waves on a SIMD alternate between MFMA and VALU phases.
 //
 constexpr int kSubKeys = 256;
 constexpr int kSubBytes = kSubKeys * 128;
