@@ -9,7 +9,8 @@ JSON line:
 plus per-stage times, indexer FP8 TFLOP/s and the 64 x 128K decode step.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload p128k]
-                       [--no-cpu-baseline] [--no-decode] [--stages-only]
+                       [--cpu-rows R] [--no-cpu-baseline] [--no-decode] [--stage-reps N]
+                       [--short-prefill-only] [--calib-copy-mb M]
 """
 from __future__ import annotations
 
@@ -108,6 +109,8 @@ def time_stages(torch, wl, d, dsa, reps, stream):
     tc = max(1, (128 << 20) // (wl.batch * S * 4))
     if tc >= 64:
         tc = tc // 32 * 32
+    if tc > 1:
+        tc &= ~1
     tc = min(tc, wl.n_q)
     sc = torch.empty((wl.batch, tc, S), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.batch, tc, k), dtype=torch.int32, device="cuda")
