@@ -314,6 +314,31 @@ def test_forward_bitwise_equals_chained_calls(name):
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
+def test_forward_split_topk_fallback_on_equal_scores():
+    # All-zero index keys make every score 0: every key is a candidate, each
+    # of the fused forward's top-k parts overflows its candidate list, and
+    # the merge takes the two-pass fallback.  Ties go to the lower index, so
+    # every row selects 0 .. k-1, as the chained calls do.
+    wl = W.custom("dec64", batch=2, n_kv=20000, q_pos0=19999)
+    d = SD.fill_inputs(wl)
+    d["k_idx"].zero_()
+    out, lse, idx = run_forward(wl, d)
+    want = torch.arange(wl.topk, dtype=torch.int32, device="cuda").expand(wl.batch, wl.n_q, wl.topk)
+    assert torch.equal(idx, want)
+    dims = dsa.Dims.of(wl)
+    sc = run_indexer(wl, d)
+    assert torch.all(sc == 0)
+    idx_c = torch.empty_like(idx)
+    dsa.dsa_topk(dims, sc, wl.n_kv, idx_c)
+    out_c, lse_c = torch.empty_like(out), torch.empty_like(lse)
+    nws = dsa.dsa_attn_workspace_size(dims)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_attn(dims, d["q"], d["kv"], idx_c, wl.sm_scale, out_c, lse_c, ws, nws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_c) and torch.equal(out, out_c)
+    assert torch.equal(lse.view(torch.int32), lse_c.view(torch.int32))
+
+
 def check_forward_rows(wl, out, lse, idx, rows_by_seq):
     worst, worst_lse, recall, amb = 0.0, 0.0, [], 0
     for b, rows in rows_by_seq.items():
