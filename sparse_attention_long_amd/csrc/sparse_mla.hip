@@ -552,9 +552,11 @@ __device__ __forceinline__ v16f qk_chunk_heads(const uint16_t* tb, const v8bf (&
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(qb[ks]), "v"(cur));
     else
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(st) : "v"(qb[ks]), "v"(cur));
+    if constexpr (CP::kPerWave > 0) {
 #pragma unroll
-    for (int jj = 0; jj < CP::kPerWave; ++jj)
-      if (jj * C::kKS / CP::kPerWave == ks) cp.issue(jj);
+      for (int jj = 0; jj < CP::kPerWave; ++jj)
+        if (jj * C::kKS / CP::kPerWave == ks) cp.issue(jj);
+    }
   }
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(st));
   return st;
