@@ -105,8 +105,8 @@ def test_attention_validation_and_workspace():
 def test_forward_workspace_plan():
     d = _dims(n_q=131072, n_kv=131072, topk=2048)
     ws = dsa.dsa_forward_workspace_size(d)
-    # 256-row chunks: 128 MiB of scores plus 2 MiB of indices
-    assert ws == 256 * 131072 * 4 + 256 * 2048 * 4
+    # 512-row chunks: 256 MiB of scores plus 4 MiB of indices
+    assert ws == 512 * 131072 * 4 + 512 * 2048 * 4
     with pytest.raises(dsa.DSAError) as e:
         dsa.dsa_forward(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE, ws=FAKE, ws_bytes=ws - 1, stream=0)
     assert e.value.status == dsa.dsa.ERR_WORKSPACE

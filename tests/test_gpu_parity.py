@@ -97,7 +97,8 @@ INDEXER_CASES = {
     "rows5": W.custom("p4k", n_q=5, n_kv=1037, q_pos0=1032),
     "decode_b3": W.custom("dec64", batch=3, n_kv=5003, q_pos0=5002),
     "decode_t3": W.custom("dec64", batch=2, n_q=3, n_kv=4099, q_pos0=4096),
-    "two_chunks": W.custom("p4k", n_q=1024, n_kv=65536, q_pos0=64512),
+    # two forward chunks at 65536 keys (1024 rows, then a ragged 512)
+    "two_chunks": W.custom("p4k", n_q=1536, n_kv=65536, q_pos0=64000),
     # few long decode rows: the fused forward spreads each row's top-k over
     # several workgroups (odd length: ragged vector split and scalar tail)
     "decode_long_b4": W.custom("dec64", batch=4, n_kv=20011, q_pos0=20010),
