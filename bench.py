@@ -105,8 +105,8 @@ def time_stages(torch, wl, d, dsa, reps, stream):
     S, k = wl.n_kv, wl.topk
     full = dsa.Dims.of(wl)
     nws = dsa.dsa_forward_workspace_size(full)
-    # chunk rows used by dsa_forward (same rule: ~256 MiB of scores per chunk)
-    tc = max(1, (256 << 20) // (wl.batch * S * 4))
+    # chunk rows used by dsa_forward (same rule: ~128 MiB of scores per chunk)
+    tc = max(1, (128 << 20) // (wl.batch * S * 4))
     if tc >= 64:
         tc = tc // 32 * 32
     if tc > 1:

@@ -130,7 +130,13 @@ int dsa_sparse_mla_attn(const dsa_dims* dims, const uint16_t* q, const uint16_t*
  *   idx_out  [B, T, topk] int32 or NULL: if given, receives the selection.
  * The result equals, bit for bit, running dsa_indexer_scores, dsa_topk and
  * dsa_sparse_mla_attn one after the other.
- * ws must hold dsa_forward_workspace_size(dims) bytes.
+ * ws must hold dsa_forward_workspace_size(dims) bytes.  When the rows span
+ * more than one chunk, the workspace holds two chunk slices, and every
+ * second chunk runs on a stream the library owns (one per device, created
+ * on first use, default priority).  That stream waits for work already
+ * enqueued on `stream`, and `stream` waits for it before the call's last
+ * operation: to the caller, the whole forward is ordered on `stream`.
+ * dsa_forward_paged and dsa_forward_kl do the same.
  */
 size_t dsa_forward_workspace_size(const dsa_dims* dims);
 int dsa_forward(const dsa_dims* dims, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,

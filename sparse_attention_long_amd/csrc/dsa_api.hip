@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
@@ -125,13 +126,14 @@ size_t attn_partial_bytes(const dsa_dims* d, int64_t rows_per_seq) {
   return (n * d->dim_v * sizeof(uint16_t) + 15) / 16 * 16 + n * sizeof(float);
 }
 
-// Query rows per chunk of dsa_forward: keep a chunk's scores near 256 MB,
-// the Infinity Cache, from which top-k reads them back.  At 128K keys that
-// is 512 rows, two rounds of the one-workgroup-per-row top-k and attention
-// launches; 128, 256, 512 and 1024 MB measured 220, 147, 142 and 151 ms per
-// 128K prefill step.
+// Query rows per chunk of dsa_forward: a chunk's scores take about 128 MB,
+// so the two chunks in flight on the two streams together fill about the
+// 256 MB Infinity Cache, from which top-k reads the scores back.  At 128K
+// keys that is 256 rows.  Measured per 128K prefill step on one box: one
+// stream with 256 MB chunks 140.6 ms; two streams with 64, 96, 128, 192 and
+// 256 MB per chunk 146.4, 143.5, 136.0, 142.0 and 138.1 ms.
 int64_t forward_chunk_rows(const dsa_dims* d) {
-  const int64_t budget = 256ll << 20;
+  const int64_t budget = 128ll << 20;
   int64_t tc = budget / ((int64_t)d->batch * d->n_kv * 4);
   if (tc >= 64) tc = tc / 32 * 32;
   if (tc > 1) tc &= ~(int64_t)1;   // even: a row keeps its indexer slot parity in every chunk
@@ -140,10 +142,16 @@ int64_t forward_chunk_rows(const dsa_dims* d) {
   return tc;
 }
 
+// A chunk's buffers (scores, selection, attention partials, top-k lists)
+// form one set of `half` bytes.  With two or more chunks the workspace holds
+// two sets: consecutive chunks alternate between the caller's stream and a
+// second stream, each with its own set, so one chunk's launches can fill the
+// tails of the other's.
 struct ForwardLayout {
   int64_t tc;
   int topk_parts;   // top-k workgroups per row (1: one per row)
-  size_t scores_off, idx_off, part_off, topk_off, total;
+  int nsets;        // 1, or 2 when the rows span more than one chunk
+  size_t scores_off, idx_off, part_off, topk_off, half, total;
 };
 
 ForwardLayout forward_layout(const dsa_dims* d) {
@@ -155,8 +163,35 @@ ForwardLayout forward_layout(const dsa_dims* d) {
   L.part_off = L.idx_off + up((size_t)d->batch * L.tc * d->topk * sizeof(int32_t));
   L.topk_off = L.part_off + up(attn_partial_bytes(d, L.tc));
   L.topk_parts = dsa::topk_split_parts((int64_t)d->batch * L.tc, d->n_kv);
-  L.total = L.topk_off + up(dsa::topk_split_bytes((int64_t)d->batch * L.tc, L.topk_parts));
+  L.half = L.topk_off + up(dsa::topk_split_bytes((int64_t)d->batch * L.tc, L.topk_parts));
+  L.nsets = d->n_q > L.tc ? 2 : 1;
+  L.total = L.nsets * L.half;
   return L;
+}
+
+// The second stream of the chunk pipeline and the two events that fork it
+// from and join it back to the caller's stream: one set per device, created
+// on first use, kept until the process ends.  The enqueue sequence holds
+// g_lane_mu, so concurrent host threads cannot interleave event records.
+struct ChunkLane {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxLaneDevices = 64;
+std::mutex g_lane_mu;
+ChunkLane g_lane[kMaxLaneDevices];
+
+hipError_t chunk_lane(ChunkLane** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxLaneDevices) return hipErrorInvalidDevice;
+  ChunkLane& c = g_lane[dev];
+  if (!c.fork && (e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess) return e;
+  if (!c.join && (e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess) return e;
+  if (!c.s2 && (e = hipStreamCreateWithFlags(&c.s2, hipStreamNonBlocking)) != hipSuccess) return e;
+  *out = &c;
+  return hipSuccess;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -320,18 +355,30 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
           L.total, ws ? ws_bytes : (size_t)0);
   REQUIRE(aligned(ws, 256), DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
-  hipStream_t s = (hipStream_t)stream;
-  char* wsb = (char*)ws;
-  float* sc = (float*)(wsb + L.scores_off);
+  const hipStream_t s0 = (hipStream_t)stream;
   const bool decode_form = d->n_q <= dsa::kIndexerDecodeMaxRows;
   const int nsplit = attn_nsplit(d);
   const int pos_base = pk.seq_lens ? 0 : d->q_pos0;
-  for (int64_t i0 = 0; i0 < d->n_q; i0 += L.tc) {
+  ChunkLane* lane = nullptr;
+  std::unique_lock<std::mutex> lk(g_lane_mu, std::defer_lock);
+  if (L.nsets > 1) {
+    lk.lock();
+    hipError_t e = chunk_lane(&lane);
+    if (e == hipSuccess) e = hipEventRecord(lane->fork, s0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(lane->s2, lane->fork, 0);
+    if (e != hipSuccess) return hip_status(e, "chunk stream fork");
+  }
+  int rc = DSA_OK;
+  for (int64_t i0 = 0, c = 0; i0 < d->n_q; i0 += L.tc, ++c) {
+    const int set = (int)(c % L.nsets);
+    const hipStream_t s = set ? lane->s2 : s0;
+    char* wsb = (char*)ws + set * L.half;
+    float* sc = (float*)(wsb + L.scores_off);
     const int rows = (int)((d->n_q - i0) < L.tc ? (d->n_q - i0) : L.tc);
     const dsa::IndexerArgs ia =
         indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, sc, d->n_kv, i0, rows, L.tc, pk);
     hipError_t e = dsa::launch_indexer(ia, decode_form, s);
-    if (e != hipSuccess) return hip_status(e, "indexer launch");
+    if (e != hipSuccess) { rc = hip_status(e, "indexer launch"); break; }
 
     dsa::TopkArgs ta{};
     ta.pk = pk;
@@ -346,7 +393,7 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     ta.S = d->n_kv;
     ta.k = d->topk;
     e = dsa::launch_topk_split(ta, L.topk_parts, wsb + L.topk_off, s);
-    if (e != hipSuccess) return hip_status(e, "top-k launch");
+    if (e != hipSuccess) { rc = hip_status(e, "top-k launch"); break; }
 
     dsa::AttnArgs aa{};
     aa.pk = pk;
@@ -372,7 +419,7 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     aa.k = d->topk;
     aa.sm_scale = sm_scale;
     e = dsa::launch_sparse_mla(aa, s);
-    if (e != hipSuccess) return hip_status(e, "attention launch");
+    if (e != hipSuccess) { rc = hip_status(e, "attention launch"); break; }
     if (kl) {
       dsa::KlArgs ka{};
       ka.at = aa;
@@ -381,10 +428,15 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
       ka.sc_rows_b = L.tc;
       ka.kl = kl + i0;
       e = dsa::launch_indexer_kl(ka, s);
-      if (e != hipSuccess) return hip_status(e, "indexer KL launch");
+      if (e != hipSuccess) { rc = hip_status(e, "indexer KL launch"); break; }
     }
   }
-  return ok();
+  if (lane) {
+    hipError_t e = hipEventRecord(lane->join, lane->s2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s0, lane->join, 0);
+    if (e != hipSuccess && rc == DSA_OK) rc = hip_status(e, "chunk stream join");
+  }
+  return rc == DSA_OK ? ok() : rc;
 }
 
 int kl_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, const uint16_t* kv, const int32_t* idx,

@@ -105,8 +105,11 @@ def test_attention_validation_and_workspace():
 def test_forward_workspace_plan():
     d = _dims(n_q=131072, n_kv=131072, topk=2048)
     ws = dsa.dsa_forward_workspace_size(d)
-    # 512-row chunks: 256 MiB of scores plus 4 MiB of indices
-    assert ws == 512 * 131072 * 4 + 512 * 2048 * 4
+    # two slices of 256-row chunks, each 128 MiB of scores plus 2 MiB of indices
+    assert ws == 2 * (256 * 131072 * 4 + 256 * 2048 * 4)
+    # rows that fit one chunk need one slice
+    one = _dims(n_q=256, n_kv=131072, q_pos0=131072 - 256, topk=2048)
+    assert dsa.dsa_forward_workspace_size(one) == 256 * 131072 * 4 + 256 * 2048 * 4
     with pytest.raises(dsa.DSAError) as e:
         dsa.dsa_forward(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE, ws=FAKE, ws_bytes=ws - 1, stream=0)
     assert e.value.status == dsa.dsa.ERR_WORKSPACE

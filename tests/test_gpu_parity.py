@@ -315,6 +315,38 @@ def test_forward_bitwise_equals_chained_calls(name):
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
+def test_forward_ordered_on_caller_stream():
+    """Rows spanning several chunks alternate between the caller's stream and
+    the library's second stream.  Work enqueued on the caller's stream just
+    before the call (the query copy) must be seen by every chunk, and work
+    enqueued just after it (the snapshots) must see every chunk's results."""
+    wl = INDEXER_CASES["two_chunks"]   # three chunks of 512 rows at 65,536 keys
+    d = SD.fill_inputs(wl)
+    ref_out, ref_lse, ref_idx = run_forward(wl, d)
+    dims = dsa.Dims.of(wl)
+    nws = dsa.dsa_forward_workspace_size(dims)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    snaps = []
+    with torch.cuda.stream(side):
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        q_in = torch.zeros_like(d["q"])
+        out, lse, idx = torch.empty_like(ref_out), torch.empty_like(ref_lse), torch.empty_like(ref_idx)
+        for rep in range(3):
+            q_in.zero_()
+            out.fill_(0)
+            idx.fill_(-1)
+            q_in.copy_(d["q"])
+            dsa.dsa_forward(dims, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], q_in, d["kv"],
+                            wl.sm_scale, out, lse, idx, ws, nws)
+            snaps.append((out.clone(), lse.clone(), idx.clone()))
+    torch.cuda.synchronize()
+    for o, l, i in snaps:
+        assert torch.equal(i, ref_idx)
+        assert torch.equal(o, ref_out)
+        assert torch.equal(l.view(torch.int32), ref_lse.view(torch.int32))
+
+
 def test_forward_split_topk_fallback_on_equal_scores():
     # All-zero index keys make every score 0: every key is a candidate, each
     # of the fused forward's top-k parts overflows its candidate list, and
