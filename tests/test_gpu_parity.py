@@ -347,6 +347,37 @@ def test_forward_ordered_on_caller_stream():
         assert torch.equal(l.view(torch.int32), ref_lse.view(torch.int32))
 
 
+def test_forward_graph_replays_match_eager():
+    """dsa_forward captured into a graph: inside the capture its chunks fork
+    onto the library's second stream and join back.  Every replay, with eager
+    work and synchronisations between replays, equals the eager call."""
+    wl = INDEXER_CASES["two_chunks"]
+    d = SD.fill_inputs(wl)
+    ref_out, ref_lse, ref_idx = run_forward(wl, d)   # eager; also creates the second stream
+    dims = dsa.Dims.of(wl)
+    nws = dsa.dsa_forward_workspace_size(dims)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    out, lse, idx = torch.empty_like(ref_out), torch.empty_like(ref_lse), torch.empty_like(ref_idx)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dsa.dsa_forward(dims, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], d["q"], d["kv"],
+                        wl.sm_scale, out, lse, idx, ws, nws)
+    for rep in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("graph replay", rep)
+        assert torch.equal(idx, ref_idx)
+        assert torch.equal(out, ref_out)
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+        o2, _, _ = run_forward(wl, d, with_idx=False)   # eager work between replays
+        assert torch.equal(o2, ref_out)
+
+
 def test_forward_split_topk_fallback_on_equal_scores():
     # All-zero index keys make every score 0: every key is a candidate, each
     # of the fused forward's top-k parts overflows its candidate list, and
