@@ -145,7 +145,12 @@ int64_t forward_chunk_rows(const dsa_dims* d) {
 // Streams of the forward's chunk pipeline: the caller's and
 // kChunkStreams - 1 that the library owns.  Three streams measured 141.0 ms
 // (128 MB chunks) and 144.5 ms (96 MB) per 128K prefill step, against
-// 139.3 ms for two on the same box.
+// 139.3 ms for two on the same box.  Two trials were dropped: a decode
+// step (64 sequences, one chunk) split into two groups of 32 sequences on
+// the two streams took 340 us against 332 us unsplit (361 us when the second
+// group's indexer waited for the first's), and starting the second stream's
+// first chunk after the first chunk's indexer left the 128K prefill step
+// unchanged (138.6 against 138.8 ms).
 constexpr int kChunkStreams = 2;
 
 // A chunk's buffers (scores, selection, attention partials, top-k lists)
