@@ -378,6 +378,49 @@ def test_forward_graph_replays_match_eager():
         assert torch.equal(o2, ref_out)
 
 
+def test_forward_from_two_host_threads():
+    """Two host threads run multi-chunk forwards at once, each on its own
+    stream and workspace.  They share the library's second stream and its
+    events (the enqueue holds a lock); every result equals the one-thread
+    result."""
+    import threading
+    wl = INDEXER_CASES["two_chunks"]
+    d = SD.fill_inputs(wl)
+    ref_out, ref_lse, ref_idx = run_forward(wl, d)
+    dims = dsa.Dims.of(wl)
+    nws = dsa.dsa_forward_workspace_size(dims)
+    bufs = [(torch.empty(nws, dtype=torch.uint8, device="cuda"), torch.empty_like(ref_out),
+             torch.empty_like(ref_lse), torch.empty_like(ref_idx), torch.cuda.Stream()) for _ in range(2)]
+    torch.cuda.synchronize()
+    errors, results = [], [[] for _ in bufs]
+
+    def worker(t):
+        try:
+            ws, out, lse, idx, st = bufs[t]
+            with torch.cuda.stream(st):
+                for _ in range(3):
+                    dsa.dsa_forward(dims, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], d["q"],
+                                    d["kv"], wl.sm_scale, out, lse, idx, ws, nws)
+                    results[t].append((out.clone(), lse.clone(), idx.clone()))
+            st.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert all(len(r) == 3 for r in results)
+    for r in results:
+        for o, l, i in r:
+            assert torch.equal(i, ref_idx)
+            assert torch.equal(o, ref_out)
+            assert torch.equal(l.view(torch.int32), ref_lse.view(torch.int32))
+
+
 def test_forward_split_topk_fallback_on_equal_scores():
     # All-zero index keys make every score 0: every key is a candidate, each
     # of the fused forward's top-k parts overflows its candidate list, and
