@@ -131,7 +131,8 @@ size_t attn_partial_bytes(const dsa_dims* d, int64_t rows_per_seq) {
 // 256 MB Infinity Cache, from which top-k reads the scores back.  At 128K
 // keys that is 256 rows.  Measured per 128K prefill step on one box: one
 // stream with 256 MB chunks 140.6 ms; two streams with 64, 96, 128, 192 and
-// 256 MB per chunk 146.4, 143.5, 136.0, 142.0 and 138.1 ms.
+// 256 MB per chunk 146.4, 143.5, 136.0, 142.0 and 138.1 ms, and on another
+// box 112, 128 and 160 MB (224, 256 and 320 rows) 141.5, 137.9 and 143.8 ms.
 int64_t forward_chunk_rows(const dsa_dims* d) {
   const int64_t budget = 128ll << 20;
   int64_t tc = budget / ((int64_t)d->batch * d->n_kv * 4);
