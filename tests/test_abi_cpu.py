@@ -110,6 +110,12 @@ def test_forward_workspace_plan():
     # rows that fit one chunk need one slice
     one = _dims(n_q=256, n_kv=131072, q_pos0=131072 - 256, topk=2048)
     assert dsa.dsa_forward_workspace_size(one) == 256 * 131072 * 4 + 256 * 2048 * 4
+    # a decode step (64 sequences, one row each) is one chunk: one slice with
+    # scores, indices, 4-way split attention partials and the top-k part lists
+    dec = _dims(batch=64, n_q=1, n_kv=131072, q_pos0=131071, topk=2048)
+    partials = 64 * 4 * 128 * (512 * 2 + 4)
+    base = 64 * 131072 * 4 + 64 * 2048 * 4 + partials
+    assert base <= dsa.dsa_forward_workspace_size(dec) < 2 * base
     with pytest.raises(dsa.DSAError) as e:
         dsa.dsa_forward(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE, ws=FAKE, ws_bytes=ws - 1, stream=0)
     assert e.value.status == dsa.dsa.ERR_WORKSPACE
