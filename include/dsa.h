@@ -76,7 +76,9 @@ typedef enum dsa_status {
  *                                      entries s >= n_p are not written.
  *   ld >= n_kv (row stride of scores, in elements).
  * Products are exact FP8 x FP8 and summed in fp32; the ReLU, head weighting
- * and head sum are done in fp32.  Scales are not validated on the device.
+ * and head sum are done in fp32.  The kernels do not check the scale values
+ * (a NaN scale gives NaN scores, which top-k ranks last); dsa_validate counts
+ * non-finite or non-positive scales on request.
  */
 int dsa_indexer_scores(const dsa_dims* dims, const uint8_t* q_idx, const float* q_scale,
                        const uint16_t* w_idx, const uint8_t* k_idx, const float* k_scale,
@@ -94,6 +96,18 @@ int dsa_indexer_scores(const dsa_dims* dims, const uint8_t* q_idx, const float* 
  * Supports n_kv <= 262144.
  */
 int dsa_topk(const dsa_dims* dims, const float* scores, int64_t ld, int32_t* idx, void* stream);
+
+/*
+ * dsa_topk with a caller workspace of dsa_topk_workspace_size(dims) bytes
+ * (256-byte aligned; the size is 0, and ws may be NULL, when no split
+ * applies).  With a workspace, few long rows (at most 128 rows of at least
+ * 16384 keys, e.g. a decode step) spread each row's candidate collection
+ * over several workgroups, as dsa_forward does for its chunks.  The
+ * selection is the same, bit for bit, as dsa_topk's.
+ */
+size_t dsa_topk_workspace_size(const dsa_dims* dims);
+int dsa_topk_ws(const dsa_dims* dims, const float* scores, int64_t ld, int32_t* idx, void* ws, size_t ws_bytes,
+                void* stream);
 
 /*
  * Sparse MLA attention in MQA mode (Eq. (2), Sec. 1.1; renormalised softmax
@@ -130,15 +144,31 @@ int dsa_sparse_mla_attn(const dsa_dims* dims, const uint16_t* q, const uint16_t*
  *   idx_out  [B, T, topk] int32 or NULL: if given, receives the selection.
  * The result equals, bit for bit, running dsa_indexer_scores, dsa_topk and
  * dsa_sparse_mla_attn one after the other.
- * ws must hold dsa_forward_workspace_size(dims) bytes.  When the rows span
- * more than one chunk, the workspace holds two chunk slices, and every
- * second chunk runs on a stream the library owns (one per device, created
- * on first use, default priority).  That stream waits for work already
- * enqueued on `stream`, and `stream` waits for it before the call's last
- * operation: to the caller, the whole forward is ordered on `stream`.
- * dsa_forward_paged and dsa_forward_kl do the same.
+ * ws must hold dsa_forward_workspace_size(dims) bytes (256-byte aligned).
+ * Every launch goes to `stream`, chunk after chunk; the call needs no host
+ * synchronisation, allocates nothing and may be captured in a HIP graph.
  */
 size_t dsa_forward_workspace_size(const dsa_dims* dims);
+
+/*
+ * How dsa_forward (and dsa_forward_paged / dsa_forward_kl) splits its work
+ * for these dims, for callers that time or reproduce its stages:
+ *   chunk_rows      query rows per chunk (the last chunk may be shorter);
+ *                   a chunk's scores are [B, chunk_rows, n_kv] f32
+ *   topk_parts      top-k workgroups per row (1; or the parts of the split
+ *                   selection that dsa_topk_ws also uses)
+ *   attn_splits     attention workgroups per row (1; or split-k partials
+ *                   merged by a log-sum-exp combine)
+ *   workspace_bytes dsa_forward_workspace_size(dims)
+ */
+typedef struct dsa_forward_plan {
+  int64_t chunk_rows;
+  int32_t topk_parts;
+  int32_t attn_splits;
+  size_t workspace_bytes;
+} dsa_forward_plan;
+int dsa_forward_plan_of(const dsa_dims* dims, dsa_forward_plan* plan);
+
 int dsa_forward(const dsa_dims* dims, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
                 const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const uint16_t* kv,
                 float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
@@ -337,6 +367,35 @@ int dsa_masked_mha_forward(const dsa_dims* dims, int32_t dim_nope, int32_t dim_v
                            const uint16_t* q_mha, const uint16_t* kv, const uint16_t* w_uk, const uint16_t* w_uv,
                            float sm_scale, uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * Opt-in device check of the inputs whose values the host cannot see (the
+ * analysis page, Sec. 5.1: check valid lengths and the finiteness of scales
+ * at kernel entry; odd scales and NaN destabilise the selection).  The
+ * stage kernels never read outside their buffers whatever these values are
+ * (lengths and page entries are clamped, NaN scores rank last); this call
+ * reports them so a caller can reject a batch.  Asynchronous on `stream`:
+ * it writes counts [8] int32 (device, 4-byte aligned, overwritten):
+ *   counts[0]  q_scale [B, n_q] entries that are NaN, infinite or <= 0
+ *   counts[1]  w_idx [B, n_q, H_I] bf16 entries that are NaN or infinite
+ *   counts[2]  k_scale entries of the tokens a query row can see (dense:
+ *              s < q_pos0 + n_q; paged: s < seq_lens[b]) that are NaN,
+ *              infinite or <= 0
+ *   counts[3]  idx [B, n_q, topk] entries that are neither -1 nor in
+ *              [0, n_p) for their row
+ *   counts[4]  idx rows not in the form dsa_topk writes (valid entries
+ *              strictly ascending, then only -1): such a row may repeat an
+ *              entry, which the attention would weigh twice
+ *   counts[5]  seq_lens entries outside [n_q, n_kv] (layout given)
+ *   counts[6]  page_table entries outside [0, num_pages) among the pages a
+ *              sequence's tokens use (layout with a page table)
+ *   counts[7]  0
+ * layout: NULL (dense caches) or a paged / variable-length layout as in the
+ * _paged calls.  Any of q_scale, w_idx, k_scale and idx may be NULL to skip
+ * its check (w_idx needs idx_heads in [1, 64]; idx needs topk).
+ */
+int dsa_validate(const dsa_dims* dims, const dsa_paged_kv* layout, const float* q_scale, const uint16_t* w_idx,
+                 const float* k_scale, const int32_t* idx, int32_t* counts, void* stream);
 
 /* Status text, thread-local last error message, ABI version (major*100+minor). */
 const char* dsa_status_string(int status);

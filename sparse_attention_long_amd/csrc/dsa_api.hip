@@ -6,7 +6,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
@@ -126,15 +125,13 @@ size_t attn_partial_bytes(const dsa_dims* d, int64_t rows_per_seq) {
   return (n * d->dim_v * sizeof(uint16_t) + 15) / 16 * 16 + n * sizeof(float);
 }
 
-// Query rows per chunk of dsa_forward: a chunk's scores take about 128 MB,
-// so the two chunks in flight on the two streams together fill about the
-// 256 MB Infinity Cache, from which top-k reads the scores back.  At 128K
-// keys that is 256 rows.  Measured per 128K prefill step on one box: one
-// stream with 256 MB chunks 140.6 ms; two streams with 64, 96, 128, 192 and
-// 256 MB per chunk 146.4, 143.5, 136.0, 142.0 and 138.1 ms, and on another
-// box 112, 128 and 160 MB (224, 256 and 320 rows) 141.5, 137.9 and 143.8 ms.
+// Query rows per chunk of dsa_forward: a chunk's scores take about 256 MiB
+// of the workspace (512 rows at 128K keys), written by the indexer and read
+// back by top-k while they are still largely in the 256 MB Infinity Cache.
+// Measured per 128K prefill step with one stream: 220, 147, 142, 146 and
+// 151 ms for 64, 128, 256, 512 and 1024 MiB per chunk.
 int64_t forward_chunk_rows(const dsa_dims* d) {
-  const int64_t budget = 128ll << 20;
+  const int64_t budget = 256ll << 20;
   int64_t tc = budget / ((int64_t)d->batch * d->n_kv * 4);
   if (tc >= 64) tc = tc / 32 * 32;
   if (tc > 1) tc &= ~(int64_t)1;   // even: a row keeps its indexer slot parity in every chunk
@@ -143,26 +140,13 @@ int64_t forward_chunk_rows(const dsa_dims* d) {
   return tc;
 }
 
-// Streams of the forward's chunk pipeline: the caller's and
-// kChunkStreams - 1 that the library owns.  Three streams measured 141.0 ms
-// (128 MB chunks) and 144.5 ms (96 MB) per 128K prefill step, against
-// 139.3 ms for two on the same box.  Two trials were dropped: a decode
-// step (64 sequences, one chunk) split into two groups of 32 sequences on
-// the two streams took 340 us against 332 us unsplit (361 us when the second
-// group's indexer waited for the first's), and starting the second stream's
-// first chunk after the first chunk's indexer left the 128K prefill step
-// unchanged (138.6 against 138.8 ms).
-constexpr int kChunkStreams = 2;
-
-// A chunk's buffers (scores, selection, attention partials, top-k lists)
-// form one set of `half` bytes.  With several chunks the workspace holds one
-// set per stream: consecutive chunks take the streams in turn, each with its
-// own set, so one chunk's launches can fill the tails of another's.
+// A chunk's buffers: scores, selection, attention partials and (for a few
+// long rows) the top-k parts' candidate lists, each 256-byte aligned.
 struct ForwardLayout {
   int64_t tc;
   int topk_parts;   // top-k workgroups per row (1: one per row)
-  int nsets;        // streams (and workspace sets) in use: min(kChunkStreams, chunks)
-  size_t scores_off, idx_off, part_off, topk_off, half, total;
+  int attn_splits;  // attention workgroups per row (1: no partials, no combine)
+  size_t scores_off, idx_off, part_off, topk_off, total;
 };
 
 ForwardLayout forward_layout(const dsa_dims* d) {
@@ -174,39 +158,9 @@ ForwardLayout forward_layout(const dsa_dims* d) {
   L.part_off = L.idx_off + up((size_t)d->batch * L.tc * d->topk * sizeof(int32_t));
   L.topk_off = L.part_off + up(attn_partial_bytes(d, L.tc));
   L.topk_parts = dsa::topk_split_parts((int64_t)d->batch * L.tc, d->n_kv);
-  L.half = L.topk_off + up(dsa::topk_split_bytes((int64_t)d->batch * L.tc, L.topk_parts));
-  const int64_t chunks = (d->n_q + L.tc - 1) / L.tc;
-  L.nsets = (int)(chunks < kChunkStreams ? (chunks < 1 ? 1 : chunks) : kChunkStreams);
-  L.total = L.nsets * L.half;
+  L.attn_splits = attn_nsplit(d);
+  L.total = L.topk_off + up(dsa::topk_split_bytes((int64_t)d->batch * L.tc, L.topk_parts));
   return L;
-}
-
-// The library's streams of the chunk pipeline and the events that fork them
-// from and join them back to the caller's stream: one set per device,
-// created on first use, kept until the process ends.  The enqueue sequence
-// holds g_lane_mu, so concurrent host threads cannot interleave event
-// records.
-struct ChunkLane {
-  hipStream_t s[kChunkStreams - 1] = {};
-  hipEvent_t fork = nullptr, join[kChunkStreams - 1] = {};
-};
-constexpr int kMaxLaneDevices = 64;
-std::mutex g_lane_mu;
-ChunkLane g_lane[kMaxLaneDevices];
-
-hipError_t chunk_lane(ChunkLane** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxLaneDevices) return hipErrorInvalidDevice;
-  ChunkLane& c = g_lane[dev];
-  if (!c.fork && (e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess) return e;
-  for (int i = 0; i < kChunkStreams - 1; ++i) {
-    if (!c.join[i] && (e = hipEventCreateWithFlags(&c.join[i], hipEventDisableTiming)) != hipSuccess) return e;
-    if (!c.s[i] && (e = hipStreamCreateWithFlags(&c.s[i], hipStreamNonBlocking)) != hipSuccess) return e;
-  }
-  *out = &c;
-  return hipSuccess;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -241,7 +195,7 @@ dsa::IndexerArgs indexer_args(const dsa_dims* d, const uint8_t* q_idx, const flo
 
 extern "C" {
 
-int dsa_version(void) { return 104; }
+int dsa_version(void) { return 200; }
 
 const char* dsa_status_string(int status) {
   switch (status) {
@@ -277,8 +231,12 @@ int indexer_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
                     "indexer launch");
 }
 
+// Top-k parts per row of a standalone call with a workspace (the rule the
+// forward applies to its chunks).
+int topk_call_parts(const dsa_dims* d) { return dsa::topk_split_parts((int64_t)d->batch * d->n_q, d->n_kv); }
+
 int topk_impl(const dsa_dims* d, const dsa::PagedKV& pk, const float* scores, int64_t ld, int32_t* idx,
-              void* stream) {
+              void* stream, void* ws = nullptr, size_t ws_bytes = 0, bool use_ws = false) {
   int st;
   if ((st = check_common(d)) != DSA_OK) return st;
   REQUIRE(scores && idx, DSA_ERR_INVALID_ARG, "null tensor pointer");
@@ -298,6 +256,14 @@ int topk_impl(const dsa_dims* d, const dsa::PagedKV& pk, const float* scores, in
   a.pos0 = pk.seq_lens ? 0 : d->q_pos0;
   a.S = d->n_kv;
   a.k = d->topk;
+  if (use_ws) {
+    const int parts = topk_call_parts(d);
+    const size_t need = dsa::topk_split_bytes((int64_t)d->batch * d->n_q, parts);
+    REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), DSA_ERR_WORKSPACE,
+            "top-k needs %zu workspace bytes (got %zu)", need, ws ? ws_bytes : (size_t)0);
+    REQUIRE(need == 0 || aligned(ws, 256), DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return hip_status(dsa::launch_topk_split(a, parts, ws, (hipStream_t)stream), "top-k launch");
+  }
   return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "top-k launch");
 }
 
@@ -370,30 +336,18 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
           L.total, ws ? ws_bytes : (size_t)0);
   REQUIRE(aligned(ws, 256), DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
-  const hipStream_t s0 = (hipStream_t)stream;
+  const hipStream_t s = (hipStream_t)stream;
   const bool decode_form = d->n_q <= dsa::kIndexerDecodeMaxRows;
-  const int nsplit = attn_nsplit(d);
+  const int nsplit = L.attn_splits;
   const int pos_base = pk.seq_lens ? 0 : d->q_pos0;
-  ChunkLane* lane = nullptr;
-  std::unique_lock<std::mutex> lk(g_lane_mu, std::defer_lock);
-  if (L.nsets > 1) {
-    lk.lock();
-    hipError_t e = chunk_lane(&lane);
-    if (e == hipSuccess) e = hipEventRecord(lane->fork, s0);
-    for (int i = 0; i + 1 < L.nsets && e == hipSuccess; ++i) e = hipStreamWaitEvent(lane->s[i], lane->fork, 0);
-    if (e != hipSuccess) return hip_status(e, "chunk stream fork");
-  }
-  int rc = DSA_OK;
-  for (int64_t i0 = 0, c = 0; i0 < d->n_q; i0 += L.tc, ++c) {
-    const int set = (int)(c % L.nsets);
-    const hipStream_t s = set ? lane->s[set - 1] : s0;
-    char* wsb = (char*)ws + set * L.half;
-    float* sc = (float*)(wsb + L.scores_off);
+  char* wsb = (char*)ws;
+  float* sc = (float*)(wsb + L.scores_off);
+  for (int64_t i0 = 0; i0 < d->n_q; i0 += L.tc) {
     const int rows = (int)((d->n_q - i0) < L.tc ? (d->n_q - i0) : L.tc);
     const dsa::IndexerArgs ia =
         indexer_args(d, q_idx, q_scale, w_idx, k_idx, k_scale, sc, d->n_kv, i0, rows, L.tc, pk);
     hipError_t e = dsa::launch_indexer(ia, decode_form, s);
-    if (e != hipSuccess) { rc = hip_status(e, "indexer launch"); break; }
+    if (e != hipSuccess) return hip_status(e, "indexer launch");
 
     dsa::TopkArgs ta{};
     ta.pk = pk;
@@ -408,7 +362,7 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     ta.S = d->n_kv;
     ta.k = d->topk;
     e = dsa::launch_topk_split(ta, L.topk_parts, wsb + L.topk_off, s);
-    if (e != hipSuccess) { rc = hip_status(e, "top-k launch"); break; }
+    if (e != hipSuccess) return hip_status(e, "top-k launch");
 
     dsa::AttnArgs aa{};
     aa.pk = pk;
@@ -434,7 +388,7 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
     aa.k = d->topk;
     aa.sm_scale = sm_scale;
     e = dsa::launch_sparse_mla(aa, s);
-    if (e != hipSuccess) { rc = hip_status(e, "attention launch"); break; }
+    if (e != hipSuccess) return hip_status(e, "attention launch");
     if (kl) {
       dsa::KlArgs ka{};
       ka.at = aa;
@@ -443,18 +397,10 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
       ka.sc_rows_b = L.tc;
       ka.kl = kl + i0;
       e = dsa::launch_indexer_kl(ka, s);
-      if (e != hipSuccess) { rc = hip_status(e, "indexer KL launch"); break; }
+      if (e != hipSuccess) return hip_status(e, "indexer KL launch");
     }
   }
-  if (lane) {
-    hipError_t e = hipSuccess;
-    for (int i = 0; i + 1 < L.nsets && e == hipSuccess; ++i) {
-      e = hipEventRecord(lane->join[i], lane->s[i]);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s0, lane->join[i], 0);
-    }
-    if (e != hipSuccess && rc == DSA_OK) rc = hip_status(e, "chunk stream join");
-  }
-  return rc == DSA_OK ? ok() : rc;
+  return ok();
 }
 
 int kl_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
@@ -506,6 +452,16 @@ int dsa_topk(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, v
   return topk_impl(d, dsa::PagedKV{}, scores, ld, idx, stream);
 }
 
+size_t dsa_topk_workspace_size(const dsa_dims* d) {
+  if (check_common(d) != DSA_OK) return 0;
+  return dsa::topk_split_bytes((int64_t)d->batch * d->n_q, topk_call_parts(d));
+}
+
+int dsa_topk_ws(const dsa_dims* d, const float* scores, int64_t ld, int32_t* idx, void* ws, size_t ws_bytes,
+                void* stream) {
+  return topk_impl(d, dsa::PagedKV{}, scores, ld, idx, stream, ws, ws_bytes, true);
+}
+
 size_t dsa_attn_workspace_size(const dsa_dims* d) {
   if (check_common(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
   return attn_partial_bytes(d, d->n_q);
@@ -519,6 +475,20 @@ int dsa_sparse_mla_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv
 size_t dsa_forward_workspace_size(const dsa_dims* d) {
   if (check_common(d) != DSA_OK || check_indexer_dims(d) != DSA_OK || check_attn_dims(d) != DSA_OK) return 0;
   return forward_layout(d).total;
+}
+
+int dsa_forward_plan_of(const dsa_dims* d, dsa_forward_plan* plan) {
+  int st;
+  if ((st = check_common(d)) != DSA_OK) return st;
+  if ((st = check_indexer_dims(d)) != DSA_OK) return st;
+  if ((st = check_attn_dims(d)) != DSA_OK) return st;
+  REQUIRE(plan != nullptr, DSA_ERR_INVALID_ARG, "plan is NULL");
+  const ForwardLayout L = forward_layout(d);
+  plan->chunk_rows = L.tc;
+  plan->topk_parts = L.topk_parts;
+  plan->attn_splits = L.attn_splits;
+  plan->workspace_bytes = L.total;
+  return ok();
 }
 
 int dsa_forward(const dsa_dims* d, const uint8_t* q_idx, const float* q_scale, const uint16_t* w_idx,
@@ -596,6 +566,39 @@ int dsa_forward_kl(const dsa_dims* d, const dsa_paged_kv* layout, const uint8_t*
 
 #undef LAYOUT_PROLOGUE
 #undef PAGED_PROLOGUE
+
+int dsa_validate(const dsa_dims* d, const dsa_paged_kv* layout, const float* q_scale, const uint16_t* w_idx,
+                 const float* k_scale, const int32_t* idx, int32_t* counts, void* stream) {
+  if (d == nullptr) return fail(DSA_ERR_INVALID_ARG, "dims is NULL");
+  dsa::PagedKV pk{};
+  dsa_dims dd = *d;
+  if (layout) {
+    dd = paged_dims(d);
+    const int st = check_paged(&dd, layout, &pk);
+    if (st != DSA_OK) return st;
+  }
+  int st;
+  if ((st = check_common(&dd)) != DSA_OK) return st;
+  REQUIRE(counts != nullptr && aligned(counts, 4), DSA_ERR_INVALID_ARG, "counts must be a 4-byte aligned device pointer");
+  REQUIRE(aligned(q_scale, 4) && aligned(k_scale, 4) && aligned(idx, 4) && aligned(w_idx, 2), DSA_ERR_INVALID_ARG,
+          "misaligned scale/weight/idx pointer");
+  REQUIRE(w_idx == nullptr || (dd.idx_heads >= 1 && dd.idx_heads <= 64), DSA_ERR_UNSUPPORTED,
+          "idx_heads must be in [1, 64] (got %d)", dd.idx_heads);
+  dsa::ValidateArgs a{};
+  a.q_scale = q_scale;
+  a.w = w_idx;
+  a.k_scale = k_scale;
+  a.idx = idx;
+  a.counts = counts;
+  a.B = dd.batch;
+  a.n_q = dd.n_q;
+  a.S = dd.n_kv;
+  a.HI = dd.idx_heads;
+  a.k = dd.topk;
+  a.q_pos0 = dd.q_pos0;
+  a.pk = pk;
+  return hip_status(dsa::launch_validate(a, (hipStream_t)stream), "validate launch");
+}
 
 int dsa_gather_stats(const dsa_dims* d, int32_t page_size, const int32_t* idx, int32_t* stats, void* stream) {
   REQUIRE(d != nullptr, DSA_ERR_INVALID_ARG, "dims is NULL");

@@ -3,7 +3,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <mutex>
+
 namespace dsa {
+
+// One-time set-up per device that host threads may reach concurrently
+// (kernel attributes, device properties): f runs once per device under
+// std::call_once and its int result is kept for later calls.
+constexpr int kMaxDevices = 64;
+struct DeviceOnce {
+  std::once_flag flag[kMaxDevices];
+  int value[kMaxDevices] = {};
+};
+// Returns f()'s kept result for the current device, or `on_error` if the
+// current device cannot be read or is beyond kMaxDevices.
+template <class F>
+int device_once(DeviceOnce& o, int on_error, F&& f) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return on_error;
+  std::call_once(o.flag[dev], [&] { o.value[dev] = f(dev); });
+  return o.value[dev];
+}
 
 // Cache layout.  Dense (both pointers null): sequence b's token s is row
 // b * S + s of the caches and every sequence holds S tokens.  Otherwise
@@ -144,6 +165,23 @@ bool mha_dims_supported(int dn, int dr, int dvh, int Dv);
 hipError_t launch_selection_mask(const MaskArgs& a, hipStream_t st);
 hipError_t launch_mha_decompress(const DecompArgs& a, hipStream_t st);
 hipError_t launch_masked_mha(const MhaArgs& a, int dn, int dr, int dvh, hipStream_t st);
+
+// Device check of inputs (counts of bad values, see dsa_validate).  Any of
+// q_scale, w, k_scale and idx may be null to skip its check; pk.seq_lens
+// null means dense caches (then key scales are checked for the tokens
+// s < q_pos0 + n_q that some query row can see).
+constexpr int kValidateCounts = 8;
+struct ValidateArgs {
+  const float* q_scale;   // [B, n_q]
+  const uint16_t* w;      // [B, n_q, HI] bf16
+  const float* k_scale;   // [B, S] or a pool
+  const int32_t* idx;     // [B, n_q, k]
+  int32_t* counts;        // [kValidateCounts]
+  int B, n_q, S, HI, k, q_pos0;
+  PagedKV pk;
+  int blocks_q, blocks_k, blocks_idx, blocks_seq;   // set by the launcher
+};
+hipError_t launch_validate(ValidateArgs a, hipStream_t st);
 
 // Shape support checks (true if the kernels are built for these dims).
 bool attn_dims_supported(int H, int Dk, int Dv);

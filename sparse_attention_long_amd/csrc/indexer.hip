@@ -741,15 +741,12 @@ bool lds_path_ok(const IndexerArgs& a) { return (2 * a.ld + (int64_t)a.S) * 4 < 
 
 // Workgroups of the LDS kernel that are resident at once: two per CU.
 int lds_slots() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cus[dev] == 0) {
+  static DeviceOnce cus;
+  return 2 * device_once(cus, 256, [](int dev) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return 2 * cus[dev];
+    return n;
+  });
 }
 
 // Key-block length of the LDS kernel.  A workgroup costs a fixed set-up

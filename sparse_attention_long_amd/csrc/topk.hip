@@ -197,8 +197,14 @@ constexpr int kCapPart = 4096;   // candidates kept per part
 // Sampled cutoff of a row: 32 blocks of 64 scores spread over the row give
 // a conservative lower bound lo for tau (the sample's rank-r 13-bit bin, r
 // chosen so that about 2m keys are expected at or above it).  hist (kBins1,
-// zero on entry) is zero again on return.
+// zero on entry) is zero again on return.  A row of fewer than 64 scores has
+// no room for the sample blocks: its cutoff is 0, the lowest key, so every
+// score becomes a candidate (n < 64 fits any candidate list).  n is
+// block-uniform, so the early return keeps the barriers uniform.
+// Sample indices: block blk starts at floor(blk (n - 64) / 31) in [0, n - 64]
+// and its 64 scores end at most at n - 1.
 __device__ __forceinline__ uint32_t sampled_cutoff(const RowSplit& row, int n, int m, uint32_t* hist, Shared& sh) {
+  if (n < 64) return 0u;
   const int t = threadIdx.x;
   const int blk = t >> 5;
   const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + 2 * (t & 31);
@@ -542,12 +548,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.rows <= 0 || a.B <= 0) return hipSuccess;
   size_t lds = 0;
   const int cap = row_cap(a, lds);
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = set_dyn_lds((const void*)topk_kernel);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static DeviceOnce attr;
+  const hipError_t ae = (hipError_t)device_once(attr, (int)hipErrorInvalidDevice,
+                                                [](int) { return (int)set_dyn_lds((const void*)topk_kernel); });
+  if (ae != hipSuccess) return ae;
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a, cap);
   return hipGetLastError();
 }
@@ -577,13 +581,13 @@ hipError_t launch_topk_split(const TopkArgs& a, int nparts, void* ws, hipStream_
   parts.nparts = nparts;
   size_t lds = 0;
   const int cap = row_cap(a, lds);
-  static bool attr_set = false;
-  if (!attr_set) {
+  static DeviceOnce attr;
+  const hipError_t ae = (hipError_t)device_once(attr, (int)hipErrorInvalidDevice, [](int) {
     hipError_t e = set_dyn_lds((const void*)topk_collect_kernel);
     if (e == hipSuccess) e = set_dyn_lds((const void*)topk_merge_kernel);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return (int)e;
+  });
+  if (ae != hipSuccess) return ae;
   const size_t lds_collect = (kBins1 + 2 * (size_t)kCapPart) * sizeof(uint32_t);
   hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)n), dim3(kThreads), lds_collect, st, a, parts);
   hipError_t e = hipGetLastError();

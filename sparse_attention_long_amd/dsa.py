@@ -23,8 +23,13 @@ EXPORTS = (
     "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged", "dsa_forward_paged",
     "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_selection_mask", "dsa_mha_decompress",
     "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size", "dsa_masked_mha_forward", "dsa_status_string",
-    "dsa_last_error", "dsa_version",
+    "dsa_last_error", "dsa_version", "dsa_topk_workspace_size", "dsa_topk_ws", "dsa_forward_plan_of",
+    "dsa_validate",
 )
+
+# dsa_validate's counters, in order.
+VALIDATE_COUNTS = ("bad_q_scale", "nonfinite_w", "bad_k_scale", "idx_out_of_range", "idx_rows_not_canonical",
+                   "seq_lens_out_of_range", "page_entries_out_of_range", "reserved")
 
 
 class DSAError(RuntimeError):
@@ -54,6 +59,12 @@ class PagedKV(ctypes.Structure):
     @classmethod
     def of(cls, seq_lens, page_table=None, page_size: int = 0, max_pages: int = 0, num_pages: int = 0):
         return cls(_ptr(seq_lens), _ptr(page_table), page_size, max_pages, num_pages)
+
+
+class ForwardPlan(ctypes.Structure):
+    """dsa_forward_plan: how dsa_forward splits its work for given dims."""
+    _fields_ = [("chunk_rows", ctypes.c_int64), ("topk_parts", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -95,13 +106,19 @@ def lib():
         L.dsa_masked_mha_workspace_size.restype = ctypes.c_size_t
         L.dsa_masked_mha_forward.argtypes = [D, I32, I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
                                              _P, _P, _P, ctypes.c_size_t, _P]
+        L.dsa_topk_workspace_size.argtypes = [D]
+        L.dsa_topk_workspace_size.restype = ctypes.c_size_t
+        L.dsa_topk_ws.argtypes = [D, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]
+        L.dsa_forward_plan_of.argtypes = [D, ctypes.POINTER(ForwardPlan)]
+        L.dsa_validate.argtypes = [D, K, _P, _P, _P, _P, _P, _P]
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.restype = ctypes.c_char_p
         for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_quantize_e4m3",
                   "dsa_cache_append", "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged",
                   "dsa_forward_paged", "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_selection_mask",
-                  "dsa_mha_decompress", "dsa_masked_mha_attn", "dsa_masked_mha_forward", "dsa_version"):
+                  "dsa_mha_decompress", "dsa_masked_mha_attn", "dsa_masked_mha_forward", "dsa_version",
+                  "dsa_topk_ws", "dsa_forward_plan_of", "dsa_validate"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -139,6 +156,28 @@ def dsa_indexer_scores(dims: Dims, q_idx, q_scale, w_idx, k_idx, k_scale, scores
 
 def dsa_topk(dims: Dims, scores, ld: int, idx, stream=None):
     _check(lib().dsa_topk(ctypes.byref(dims), _ptr(scores), int(ld), _ptr(idx), _stream(stream)))
+
+
+def dsa_topk_workspace_size(dims: Dims) -> int:
+    return int(lib().dsa_topk_workspace_size(ctypes.byref(dims)))
+
+
+def dsa_topk_ws(dims: Dims, scores, ld: int, idx, ws=None, ws_bytes: int = 0, stream=None):
+    _check(lib().dsa_topk_ws(ctypes.byref(dims), _ptr(scores), int(ld), _ptr(idx), _ptr(ws), int(ws_bytes),
+                             _stream(stream)))
+
+
+def dsa_forward_plan_of(dims: Dims) -> ForwardPlan:
+    plan = ForwardPlan()
+    _check(lib().dsa_forward_plan_of(ctypes.byref(dims), ctypes.byref(plan)))
+    return plan
+
+
+def dsa_validate(dims: Dims, layout, q_scale, w_idx, k_scale, idx, counts, stream=None):
+    """layout: a PagedKV, or None for dense caches; any input may be None to
+    skip its check.  counts: device int32 [8] (see VALIDATE_COUNTS)."""
+    _check(lib().dsa_validate(ctypes.byref(dims), ctypes.byref(layout) if layout is not None else None,
+                              _ptr(q_scale), _ptr(w_idx), _ptr(k_scale), _ptr(idx), _ptr(counts), _stream(stream)))
 
 
 def dsa_attn_workspace_size(dims: Dims) -> int:
