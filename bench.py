@@ -6,11 +6,12 @@ JSON line:
   value        query-tokens/s of dsa_forward on the 128K prefill workload
   roofline     the dominant kernel's algorithmic throughput against its peak
   cpu_baseline the CPU oracle on a stratified row sample of the same workload
-plus per-stage times, indexer FP8 TFLOP/s and the 64 x 128K decode step.
+plus per-stage times, indexer FP8 TFLOP/s, the 32K prefill, the 64 x 128K
+decode step and the other legs (paged decode, quantisation, short prefill).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload p128k]
-                       [--cpu-rows R] [--no-cpu-baseline] [--no-decode] [--stage-reps N]
-                       [--short-prefill-only] [--calib-copy-mb M]
+                       [--cpu-rows R] [--cpu-decode-seqs N] [--no-cpu-baseline] [--no-decode]
+                       [--stage-reps N] [--short-prefill-only] [--calib-copy-mb M]
 """
 from __future__ import annotations
 
@@ -99,31 +100,28 @@ def time_forward_kl(torch, wl, d, dsa, steps, warmup, stream):
 
 
 def time_stages(torch, wl, d, dsa, reps, stream):
-    """The forward's chunk loop through the three separate calls (bit-identical
-    launches), with events between stages: per-kernel average durations."""
-    import synth.workloads as W  # noqa: F401
+    """The forward's chunk loop through the three separate calls, with events
+    between stages: the chunk rows and the top-k split come from the
+    library's own plan (dsa_forward_plan_of), so every launch is the one
+    dsa_forward makes.  Returns per-stage times, launches per stage and the
+    forward's workspace size."""
     S, k = wl.n_kv, wl.topk
     full = dsa.Dims.of(wl)
-    nws = dsa.dsa_forward_workspace_size(full)
-    # chunk rows used by dsa_forward (same rule: ~128 MiB of scores per chunk)
-    tc = max(1, (128 << 20) // (wl.batch * S * 4))
-    if tc >= 64:
-        tc = tc // 32 * 32
-    if tc > 1:
-        tc &= ~1
-    tc = min(tc, wl.n_q)
+    plan = dsa.dsa.dsa_forward_plan_of(full)
+    tc = int(plan.chunk_rows)
     sc = torch.empty((wl.batch, tc, S), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.batch, tc, k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.batch, wl.n_q, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
     lse = torch.empty((wl.batch, wl.n_q, wl.heads), dtype=torch.float32, device="cuda")
     assert wl.batch == 1 or tc == wl.n_q
-    anws = dsa.dsa_attn_workspace_size(full)
+    anws = dsa.dsa_attn_workspace_size(dsa.Dims.of(wl, n_q=tc))
     aws = torch.empty(max(anws, 1), dtype=torch.uint8, device="cuda")
+    tnws = dsa.dsa.dsa_topk_workspace_size(dsa.Dims.of(wl, n_q=tc))
+    tws = torch.empty(max(tnws, 1), dtype=torch.uint8, device="cuda")
     t = Timer(torch, stream)
     tot = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
     launches = 0
     s = stream.cuda_stream
-    HI, dI, H, Dk, Dv = wl.idx_heads, wl.idx_dim, wl.heads, wl.dim_qk, wl.dim_v
     for _ in range(reps):
         for i0 in range(0, wl.n_q, tc):
             rows = min(tc, wl.n_q - i0)
@@ -136,9 +134,8 @@ def time_stages(torch, wl, d, dsa, reps, stream):
             e0 = t.event()
             dsa.dsa_indexer_scores(cd, qi, qs, w, d["k_idx"], d["k_scale"], sc, S, stream=s)
             e1 = t.event()
-            dsa.dsa_topk(cd, sc, S, idx, stream=s)
+            dsa.dsa.dsa_topk_ws(cd, sc, S, idx, tws, tnws, stream=s)
             e2 = t.event()
-            # attention of a chunk uses the workload's split rule, as dsa_forward does
             dsa.dsa_sparse_mla_attn(cd, q, d["kv"], idx, wl.sm_scale, o, l, aws, anws, stream=s)
             e3 = t.event()
             torch.cuda.synchronize()
@@ -146,7 +143,7 @@ def time_stages(torch, wl, d, dsa, reps, stream):
             tot["topk"] += e1.elapsed_time(e2)
             tot["attention"] += e2.elapsed_time(e3)
             launches += 1
-    return {k2: v / reps for k2, v in tot.items()}, launches // reps, nws
+    return {k2: v / reps for k2, v in tot.items()}, launches // reps, int(plan.workspace_bytes)
 
 
 # Dominant-kernel names per stage, the rocprofv3 summary that holds its
@@ -410,18 +407,38 @@ def hbm_copy_rate(torch, mib=1024, reps=5):
     return {"GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "bytes_copied": n}
 
 
-def cpu_baseline(wl, n_rows):
-    """The CPU oracle (unchanged) on a stratified sample of query rows:
-    rows i_r = floor((r + 1/2) L / R).  Input generation is not timed."""
-    from oracle import dsa_oracle as O
-    from synth import workloads as W
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    L = wl.n_q
-    rows = [int((r + 0.5) * L / n_rows) for r in range(n_rows)]
+        return os.cpu_count() or 1
+
+
+def stratified(L, n_rows):
+    return [int((r + 0.5) * L / n_rows) for r in range(n_rows)]
+
+
+def cpu_baseline(wl, n_rows, gpu_sel=None):
+    """The CPU oracle (unchanged) on a stratified sample of query rows
+    floor((r + 1/2) L / R), each stage timed separately.  Input generation is
+    not timed.  With gpu_sel (the GPU's selection of those rows), also the
+    set recall R_k = |T_k n S_k| / k of the GPU set against the oracle set
+    (Sec. 5, Eq. (14)) and the oracle's cutoff margin s_(k) - s_(k+1)
+    (Sec. 5.2, Eq. (18)) over the sampled rows."""
+    from oracle import dsa_oracle as O
+    from synth import workloads as W
+    rows = stratified(wl.n_q, n_rows)
     c, s = W.k_idx_fp8(wl, 0, 0, wl.n_kv)
     k_all = O.dequant_e4m3(c, s)
     kv = O.bf16_decode(W.kv_bf16_rows(wl, 0, np.arange(wl.n_kv)))
@@ -429,13 +446,74 @@ def cpu_baseline(wl, n_rows):
     qi = O.dequant_e4m3(qc, qs)
     w = O.bf16_decode(W.w_idx_bf16(wl, 0, rows))
     q = O.bf16_decode(W.q_bf16(wl, 0, rows))
-    t0 = time.perf_counter()
+    st = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    recall, margins = [], []
     for n, i in enumerate(rows):
-        O.dsa_row(qi[n], w[n], k_all, q[n], kv, wl.q_pos0 + i, wl.topk, wl.sm_scale, wl.dim_v)
-    dt = time.perf_counter() - t0
-    return {"value": n_rows / dt, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_rows} stratified query rows of {wl.name} (rows floor((r+1/2)L/{n_rows})), "
-                      f"float64 numpy, {dt:.1f} s timed; input generation excluded"}
+        p = wl.q_pos0 + i
+        t0 = time.perf_counter()
+        sc = O.indexer_row(qi[n], w[n], k_all, p)
+        t1 = time.perf_counter()
+        sel = O.topk_row(sc, wl.topk)
+        t2 = time.perf_counter()
+        O.sparse_mla_row(q[n], kv, sel, wl.sm_scale, wl.dim_v)
+        t3 = time.perf_counter()
+        st["indexer"] += t1 - t0
+        st["topk"] += t2 - t1
+        st["attention"] += t3 - t2
+        if gpu_sel is not None and sc.size > wl.topk:
+            ref = sel[sel >= 0]
+            g = gpu_sel[n][gpu_sel[n] >= 0]
+            recall.append(np.intersect1d(ref, g).size / ref.size)
+            srt = np.sort(sc.astype(np.float64))[::-1]
+            margins.append(float(srt[wl.topk - 1] - srt[wl.topk]))
+    dt = sum(st.values())
+    res = {"value": n_rows / dt, "unit": "query-tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{n_rows} stratified query rows of {wl.name} (rows floor((r+1/2)L/{n_rows})), "
+                     f"float64 numpy, {dt:.1f} s timed; input generation excluded",
+           "stage_s": st}
+    if recall:
+        m = np.array(margins)
+        edges = [0.0, 1e-6, 1e-5, 1e-4, 1e-3, 1e-2, 1e-1, np.inf]
+        res["selection_vs_oracle"] = {
+            "rows": len(recall), "recall_mean": float(np.mean(recall)), "recall_min": float(np.min(recall)),
+            "margin_quantiles": {str(qq): float(np.quantile(m, qq)) for qq in (0.0, 0.01, 0.5, 0.99)},
+            "margin_hist": {f"[{a:g},{b:g})": int(x) for a, b, x in zip(edges[:-1], edges[1:],
+                                                                         np.histogram(m, edges)[0])}}
+    return res
+
+
+def cpu_baseline_decode(dw, n_seq):
+    """The CPU oracle on the first n_seq sequences of the decode step (one
+    query row each against its own 128K cache), each stage timed."""
+    from oracle import dsa_oracle as O
+    from synth import workloads as W
+    st = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    for b in range(n_seq):
+        c, s = W.k_idx_fp8(dw, b, 0, dw.n_kv)
+        k_all = O.dequant_e4m3(c, s)
+        qc, qs = W.q_idx_fp8(dw, b, [0])
+        qi = O.dequant_e4m3(qc, qs)[0]
+        w = O.bf16_decode(W.w_idx_bf16(dw, b, [0]))[0]
+        q = O.bf16_decode(W.q_bf16(dw, b, [0]))[0]
+        t0 = time.perf_counter()
+        sc = O.indexer_row(qi, w, k_all, dw.q_pos0)
+        t1 = time.perf_counter()
+        sel = O.topk_row(sc, dw.topk)
+        t2 = time.perf_counter()
+        kv = O.bf16_decode(W.kv_bf16_rows(dw, b, sel))
+        t2b = time.perf_counter()
+        O.sparse_mla_row(q, kv, np.arange(sel.size), dw.sm_scale, dw.dim_v)
+        t3 = time.perf_counter()
+        st["indexer"] += t1 - t0
+        st["topk"] += t2 - t1
+        st["attention"] += t3 - t2b
+    dt = sum(st.values())
+    return {"value": n_seq / dt, "unit": "decode query-tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{n_seq} of the 64 sequences of {dw.name} (one query row each), float64 numpy, "
+                      f"{dt:.2f} s timed; input generation and the selected rows' generation excluded",
+            "stage_s": st}
 
 
 def main():
@@ -447,6 +525,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="stratified query rows the CPU oracle baseline times (1024: about 10 s on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-decode-seqs", type=int, default=2,
+                    help="decode sequences the CPU oracle times per stage (each regenerates its 128K key cache)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=1)
     ap.add_argument("--short-prefill-only", action="store_true",
@@ -516,6 +596,18 @@ def main():
     roof["launches"] = launches
     roof["avg_launch_us"] = stages[dom] * 1e3 / max(launches, 1)
 
+    gpu_sel = None
+    if not args.no_cpu_baseline:
+        # the GPU's selection of the rows the CPU oracle samples (an untimed forward with idx_out)
+        dims, out, lse, ws, nws = alloc_forward(torch, wl, dsa)
+        idx_all = torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device="cuda")
+        dsa.dsa_forward(dims, d["q_idx"], d["q_scale"], d["w_idx"], d["k_idx"], d["k_scale"], d["q"], d["kv"],
+                        wl.sm_scale, out, lse, idx_all, ws, nws, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        gpu_sel = idx_all[0, stratified(wl.n_q, args.cpu_rows)].cpu().numpy()
+        del dims, out, lse, ws, idx_all
+        torch.cuda.empty_cache()
+
     train = None
     if not args.no_decode:
         log("[bench] sparse-stage training forward (dsa_forward_kl)")
@@ -528,6 +620,24 @@ def main():
         log(f"[bench] training forward {train}")
     del d
     torch.cuda.empty_cache()
+
+    p32k = None
+    if not args.no_decode and wl.name != "p32k":
+        pw = W.WORKLOADS["p32k"]
+        log("[bench] prefill p32k (low-rank latents)")
+        pd = fill_inputs(pw)
+        torch.cuda.synchronize()
+        pms = time_forward(torch, pw, pd, dsa, max(args.steps, 3), 1, stream)
+        pst, _, _ = time_stages(torch, pw, pd, dsa, 1, stream)
+        p32k = {"workload": "p32k", "ms_per_step": pms, "query_tokens_per_s": pw.n_q / (pms / 1e3),
+                "stages_ms": pst,
+                "indexer_fp8_tflops": pw.indexer_flop() / (pst["indexer"] / 1e3) / 1e12,
+                "attention_bf16_tflops": pw.attn_flop() / (pst["attention"] / 1e3) / 1e12,
+                "topk_GB_per_s": (4.0 * pw.causal_pairs() + 4.0 * pw.n_q * pw.topk) / (pst["topk"] / 1e3) / 1e9,
+                "roofline_sum": roofline_sum(pw, pms)}
+        log(f"[bench] p32k {p32k}")
+        del pd
+        torch.cuda.empty_cache()
 
     decode = None
     if not args.no_decode:
@@ -549,6 +659,8 @@ def main():
                   "mla_gather_GB_per_s": mla_bytes / (dstages["attention"] / 1e3) / 1e9,
                   "algorithmic_bytes_per_step": step_bytes}
         decode["mla_frac_of_hbm_peak"] = decode["mla_gather_GB_per_s"] / PEAK_HBM_GBS
+        decode["plan"] = {"topk_parts": int(dsa.dsa.dsa_forward_plan_of(dsa.Dims.of(dw)).topk_parts),
+                          "attn_splits": int(dsa.dsa.dsa_forward_plan_of(dsa.Dims.of(dw)).attn_splits)}
         log(f"[bench] decode {dms*1e3:.1f} us/step; {decode}")
         del dd
         torch.cuda.empty_cache()
@@ -577,8 +689,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_rows} rows")
-        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu = cpu_baseline(wl, args.cpu_rows, gpu_sel)
         log(f"[bench] cpu {cpu}")
+        if not args.no_decode and args.cpu_decode_seqs > 0:
+            cpu["decode"] = cpu_baseline_decode(W.WORKLOADS["dec64"], args.cpu_decode_seqs)
+            log(f"[bench] cpu decode {cpu['decode']}")
 
     res = {
         "metric": METRIC, "value": toks, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -589,7 +704,7 @@ def main():
                    "dim_v": wl.dim_v},
         "stages_ms": stages, "indexer_fp8_tflops": idx_tflops, "attention_bf16_tflops": attn_tflops,
         "topk_GB_per_s": topk_gbs, "roofline": roof, "train_forward_kl": train, "decode": decode,
-        "decode_paged": decode_paged, "short_prefill": short,
+        "p32k": p32k, "decode_paged": decode_paged, "short_prefill": short,
         "quantize": quant, "cpu_baseline": cpu, "roofline_sum": roofline_sum(wl, ms),
         "hbm_copy": hbm_copy_rate(torch),
     }

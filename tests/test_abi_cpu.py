@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sparse_attention_long_amd as dsa
@@ -27,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert dsa.dsa_version() == 104
+    assert dsa.dsa_version() == 200
     L = dsa.lib()
     assert L.dsa_status_string(0) == b"ok"
     assert L.dsa_status_string(3) == b"workspace too small"
@@ -105,17 +106,32 @@ def test_attention_validation_and_workspace():
 def test_forward_workspace_plan():
     d = _dims(n_q=131072, n_kv=131072, topk=2048)
     ws = dsa.dsa_forward_workspace_size(d)
-    # two slices of 256-row chunks, each 128 MiB of scores plus 2 MiB of indices
-    assert ws == 2 * (256 * 131072 * 4 + 256 * 2048 * 4)
-    # rows that fit one chunk need one slice
+    # one 512-row chunk: 256 MiB of scores plus 4 MiB of indices
+    assert ws == 512 * 131072 * 4 + 512 * 2048 * 4
+    plan = dsa.dsa.dsa_forward_plan_of(d)
+    assert (plan.chunk_rows, plan.topk_parts, plan.attn_splits, plan.workspace_bytes) == (512, 1, 1, ws)
+    # fewer rows than a chunk: the chunk shrinks to them
     one = _dims(n_q=256, n_kv=131072, q_pos0=131072 - 256, topk=2048)
     assert dsa.dsa_forward_workspace_size(one) == 256 * 131072 * 4 + 256 * 2048 * 4
-    # a decode step (64 sequences, one row each) is one chunk: one slice with
-    # scores, indices, 4-way split attention partials and the top-k part lists
+    # a decode step (64 sequences, one row each) is one chunk with scores,
+    # indices, 4-way split attention partials and the top-k part lists
     dec = _dims(batch=64, n_q=1, n_kv=131072, q_pos0=131071, topk=2048)
     partials = 64 * 4 * 128 * (512 * 2 + 4)
     base = 64 * 131072 * 4 + 64 * 2048 * 4 + partials
     assert base <= dsa.dsa_forward_workspace_size(dec) < 2 * base
+    plan = dsa.dsa.dsa_forward_plan_of(dec)
+    assert (plan.chunk_rows, plan.topk_parts, plan.attn_splits) == (1, 4, 4)
+    assert plan.workspace_bytes == dsa.dsa_forward_workspace_size(dec)
+    # the standalone top-k with a workspace splits the same way
+    assert dsa.dsa.dsa_topk_workspace_size(dec) == dsa.dsa_forward_workspace_size(dec) - base
+    assert dsa.dsa.dsa_topk_workspace_size(d) == 0
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa.dsa_topk_ws(dec, FAKE, 131072, FAKE, ws=FAKE, ws_bytes=dsa.dsa.dsa_topk_workspace_size(dec) - 1,
+                            stream=0)
+    assert e.value.status == dsa.dsa.ERR_WORKSPACE
+    with pytest.raises(dsa.DSAError) as e:
+        dsa.dsa.dsa_forward_plan_of(_dims(heads=7, dim_qk=100))   # dim_v 512 > dim_qk 100
+    assert e.value.status == dsa.dsa.ERR_INVALID_ARG
     with pytest.raises(dsa.DSAError) as e:
         dsa.dsa_forward(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE, ws=FAKE, ws_bytes=ws - 1, stream=0)
     assert e.value.status == dsa.dsa.ERR_WORKSPACE
@@ -250,3 +266,32 @@ def test_masked_mha_workspace_plan():
         D.dsa_masked_mha_forward(d, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.07, FAKE,
                                  ws=FAKE, ws_bytes=ws - 1, stream=0)
     assert e.value.status == D.ERR_WORKSPACE
+
+
+def test_validate_host_checks():
+    D = dsa.dsa
+    d = _dims(batch=2, n_q=1, n_kv=200, topk=16)
+    for kw, status in ((dict(counts=None), D.ERR_INVALID_ARG), (dict(counts=FAKE + 2), D.ERR_INVALID_ARG),
+                       (dict(q_scale=FAKE + 2), D.ERR_INVALID_ARG), (dict(idx=FAKE + 1), D.ERR_INVALID_ARG)):
+        a = dict(q_scale=FAKE, w_idx=FAKE, k_scale=FAKE, idx=FAKE, counts=FAKE)
+        a.update(kw)
+        with pytest.raises(dsa.DSAError) as e:
+            D.dsa_validate(d, None, a["q_scale"], a["w_idx"], a["k_scale"], a["idx"], a["counts"], stream=0)
+        assert e.value.status == status
+    with pytest.raises(dsa.DSAError) as e:   # the dims are checked as in the other calls
+        D.dsa_validate(_dims(q_pos0=1), None, FAKE, None, None, None, FAKE, stream=0)
+    assert e.value.status == D.ERR_INVALID_ARG
+    with pytest.raises(dsa.DSAError) as e:   # and a paged layout as in the _paged calls
+        D.dsa_validate(d, _layout(page_size=32), FAKE, None, None, None, FAKE, stream=0)
+    assert e.value.status == D.ERR_UNSUPPORTED
+    assert len(D.VALIDATE_COUNTS) == 8
+
+
+def test_topk_sample_indices_stay_inside_the_row():
+    """The top-k kernel's sampled cutoff reads 32 blocks of 64 scores at
+    e = floor(blk (n - 64) / 31) + j, j < 64, for rows of n >= 64 scores
+    (shorter rows take no sample): every index lies in [0, n)."""
+    for n in list(range(64, 5000)) + [131071, 131072, 262144]:
+        blk = np.arange(32, dtype=np.int64)
+        first = (blk * (n - 64)) // 31
+        assert first.min() >= 0 and (first + 63).max() <= n - 1, n

@@ -513,3 +513,57 @@ def test_masked_mha_single_key_and_empty_rows():
 def test_selection_mask_bits():
     m = O.selection_mask(np.array([0, 3, 3, 31, 32, -1, 40, 7]), 33)
     assert np.flatnonzero(m).tolist() == [0, 3, 7, 31, 32]
+
+
+# ----------------------------------------------------------------- dequantisation and cache append
+def test_dequant_scale_multiplies_each_token():
+    """One scale per token: the scale of token t multiplies every value of
+    token t (and nothing of another token), for 2-D and 3-D code arrays.
+    Codes from the OCP E4M3 table: 0x38 = 1, 0x40 = 2, 0xB8 = -1, 0x30 = 0.5."""
+    codes = np.array([[0x38, 0x40, 0xB8], [0x38, 0x40, 0xB8]], np.uint8)   # 2 tokens x 3 values
+    got = O.dequant_e4m3(codes, np.array([2.0, 0.5], np.float32))
+    assert np.array_equal(got, [[2.0, 4.0, -2.0], [0.5, 1.0, -0.5]])
+    codes3 = np.array([[[0x38, 0x30], [0x40, 0x38]], [[0xB8, 0x40], [0x30, 0x30]]], np.uint8)   # [B=2, T=2, d=2]
+    scales3 = np.array([[1.0, 2.0], [4.0, 8.0]], np.float32)
+    want3 = np.array([[[1.0, 0.5], [4.0, 2.0]], [[-4.0, 8.0], [4.0, 4.0]]])
+    assert np.array_equal(O.dequant_e4m3(codes3, scales3), want3)
+
+
+def _cache_append_golden(golden_dir):
+    rows = []
+    for line in open(f"{golden_dir}/cache_append_worked.txt"):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        lhs, sc, codes = (x.strip() for x in line.split("|"))
+        f = lhs.split()
+        rows.append((int(f[0]), int(f[1]), [float(v) for v in f[2:]], float(sc), [int(c, 16) for c in codes.split()]))
+    return rows
+
+
+def test_cache_append_worked_example(golden_dir):
+    """Rows pos0 .. pos0 + n - 1 of every sequence receive the new tokens'
+    codes, scales and latents; every other row keeps its old contents."""
+    B, S, d, pos0, n = 2, 5, 4, 2, 2
+    gold = _cache_append_golden(golden_dir)
+    k_new = np.zeros((B, n, d), np.float32)
+    for b, t, x, _, _ in gold:
+        k_new[b, t] = x
+    kv_new = np.arange(B * n * 3, dtype=np.float64).reshape(B, n, 3) + 100.0
+    kc0 = np.full((B, S, d), 0x11, np.uint8)
+    ks0 = np.full((B, S), 3.0, np.float32)
+    kv0 = np.full((B, S, 3), 9.0)
+    kc, ks, kv = O.cache_append(kc0, ks0, kv0, k_new, kv_new, pos0)
+    for b, t, _, scale, codes in gold:
+        assert np.array_equal(kc[b, pos0 + t], codes), (b, t)
+        assert ks[b, pos0 + t] == np.float32(scale), (b, t)
+        assert np.array_equal(kv[b, pos0 + t], kv_new[b, t])
+    other = [r for r in range(S) if not pos0 <= r < pos0 + n]
+    assert np.all(kc[:, other] == 0x11) and np.all(ks[:, other] == 3.0) and np.all(kv[:, other] == 9.0)
+    # the inputs are not modified, and the codes are those of the quantiser
+    assert np.all(kc0 == 0x11) and np.all(ks0 == 3.0) and np.all(kv0 == 9.0)
+    codes_q, scales_q = O.quantize_e4m3_tokens(k_new)
+    assert np.array_equal(kc[:, pos0:pos0 + n], codes_q) and np.array_equal(ks[:, pos0:pos0 + n], scales_q)
+    # without latents only the key caches change
+    kc2, ks2, kv2 = O.cache_append(kc0, ks0, None, k_new, None, pos0)
+    assert kv2 is None and np.array_equal(kc2, kc) and np.array_equal(ks2, ks)
