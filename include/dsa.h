@@ -136,6 +136,23 @@ int dsa_sparse_mla_attn(const dsa_dims* dims, const uint16_t* q, const uint16_t*
                         void* stream);
 
 /*
+ * dsa_sparse_mla_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split partials that
+ * dsa_attn_workspace_size(dims) bytes would hold live in a static device
+ * array of the library instead: 40 MiB per GPU, held from the first use of
+ * the library on that GPU until the process ends (the 64-row decode step at
+ * 128 heads x 512 dims needs 33.7 MB).  Dims needing more return
+ * DSA_ERR_UNSUPPORTED before any launch.  The call allocates nothing; its
+ * results equal dsa_sparse_mla_attn's bit for bit.  Every call on one GPU
+ * shares that array: calls that may overlap in time on one GPU (on
+ * different streams without ordering between them) race and must not be
+ * issued; calls ordered on one stream are safe.
+ */
+int dsa_sparse_mla_attn_noalloc(const dsa_dims* dims, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                float sm_scale, uint16_t* out, float* lse, void* stream);
+
+/*
  * The whole forward path: indexer -> top-k -> sparse MLA, processed in
  * chunks of query rows so that each chunk's scores stay in a workspace
  * slice (the workspace also holds the selection, the attention's split

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
@@ -403,6 +404,33 @@ int forward_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint8_t* q_idx
   return ok();
 }
 
+// ---- the no-allocation attention call: its split partials live in a
+// static device array instead of a caller workspace.  `scratch` names the
+// array only in device code; host code uses the address that
+// hipGetSymbolAddress returns for the current device (each device holds its
+// own copy), taken once per device on the first call there.
+constexpr size_t kNoAllocScratchBytes = 40ull << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+struct ScratchAddr {
+  std::once_flag flag[dsa::kMaxDevices];
+  void* ptr[dsa::kMaxDevices] = {};
+  hipError_t err[dsa::kMaxDevices] = {};
+};
+ScratchAddr g_scratch;
+
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= dsa::kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch.flag[dev], [dev] {
+    g_scratch.err[dev] = hipGetSymbolAddress(&g_scratch.ptr[dev], HIP_SYMBOL(scratch));
+  });
+  *out = g_scratch.ptr[dev];
+  return g_scratch.err[dev];
+}
+
 int kl_impl(const dsa_dims* d, const dsa::PagedKV& pk, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
             const float* lse, const float* scores, int64_t ld, float sm_scale, float* kl, void* stream) {
   int st;
@@ -470,6 +498,24 @@ size_t dsa_attn_workspace_size(const dsa_dims* d) {
 int dsa_sparse_mla_attn(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                         float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return attn_impl(d, dsa::PagedKV{}, q, kv, idx, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int dsa_sparse_mla_attn_noalloc(const dsa_dims* d, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                float sm_scale, uint16_t* out, float* lse, void* stream) {
+  int st;
+  if ((st = validate_attn(d, q, kv, idx, sm_scale, out, lse, true, true)) != DSA_OK) return st;
+  const size_t need = attn_partial_bytes(d, d->n_q);
+  REQUIRE(need <= kNoAllocScratchBytes, DSA_ERR_UNSUPPORTED,
+          "these dims need %zu bytes of split partials; the no-allocation call holds at most %zu (use "
+          "dsa_sparse_mla_attn with a workspace)",
+          need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_status(e, "scratch address");
+  }
+  return attn_impl(d, dsa::PagedKV{}, q, kv, idx, sm_scale, out, lse, ws, need > 0 ? kNoAllocScratchBytes : 0,
+                   stream);
 }
 
 size_t dsa_forward_workspace_size(const dsa_dims* d) {

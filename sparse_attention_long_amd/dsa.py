@@ -24,7 +24,7 @@ EXPORTS = (
     "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_selection_mask", "dsa_mha_decompress",
     "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size", "dsa_masked_mha_forward", "dsa_status_string",
     "dsa_last_error", "dsa_version", "dsa_topk_workspace_size", "dsa_topk_ws", "dsa_forward_plan_of",
-    "dsa_validate",
+    "dsa_validate", "dsa_sparse_mla_attn_noalloc",
 )
 
 # dsa_validate's counters, in order.
@@ -111,6 +111,7 @@ def lib():
         L.dsa_topk_ws.argtypes = [D, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]
         L.dsa_forward_plan_of.argtypes = [D, ctypes.POINTER(ForwardPlan)]
         L.dsa_validate.argtypes = [D, K, _P, _P, _P, _P, _P, _P]
+        L.dsa_sparse_mla_attn_noalloc.argtypes = [D, _P, _P, _P, ctypes.c_float, _P, _P, _P]
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -118,7 +119,7 @@ def lib():
                   "dsa_cache_append", "dsa_indexer_scores_paged", "dsa_topk_paged", "dsa_sparse_mla_attn_paged",
                   "dsa_forward_paged", "dsa_gather_stats", "dsa_indexer_kl", "dsa_forward_kl", "dsa_selection_mask",
                   "dsa_mha_decompress", "dsa_masked_mha_attn", "dsa_masked_mha_forward", "dsa_version",
-                  "dsa_topk_ws", "dsa_forward_plan_of", "dsa_validate"):
+                  "dsa_topk_ws", "dsa_forward_plan_of", "dsa_validate", "dsa_sparse_mla_attn_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -188,6 +189,11 @@ def dsa_sparse_mla_attn(dims: Dims, q, kv, idx, sm_scale: float, out, lse=None, 
                         stream=None):
     _check(lib().dsa_sparse_mla_attn(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), float(sm_scale), _ptr(out),
                                      _ptr(lse), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def dsa_sparse_mla_attn_noalloc(dims: Dims, q, kv, idx, sm_scale: float, out, lse=None, stream=None):
+    _check(lib().dsa_sparse_mla_attn_noalloc(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), float(sm_scale),
+                                             _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def dsa_forward_workspace_size(dims: Dims) -> int:

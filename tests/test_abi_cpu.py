@@ -295,3 +295,19 @@ def test_topk_sample_indices_stay_inside_the_row():
         blk = np.arange(32, dtype=np.int64)
         first = (blk * (n - 64)) // 31
         assert first.min() >= 0 and (first + 63).max() <= n - 1, n
+
+
+def test_noalloc_attention_limit():
+    D = dsa.dsa
+    # 255 rows split two ways need 67 MB of partials: above the 40 MiB array
+    d = _dims(batch=255, n_q=1, n_kv=131072, q_pos0=131071, topk=2048)
+    assert dsa.dsa_attn_workspace_size(d) > 40 << 20
+    with pytest.raises(dsa.DSAError) as e:
+        D.dsa_sparse_mla_attn_noalloc(d, FAKE, FAKE, FAKE, 0.1, FAKE, stream=0)
+    assert e.value.status == D.ERR_UNSUPPORTED and "at most" in str(e.value)
+    # the 64-row decode step fits
+    assert dsa.dsa_attn_workspace_size(_dims(batch=64, n_q=1, n_kv=131072, q_pos0=131071, topk=2048)) <= 40 << 20
+    # the other checks are those of dsa_sparse_mla_attn
+    with pytest.raises(dsa.DSAError) as e:
+        D.dsa_sparse_mla_attn_noalloc(_dims(), FAKE, FAKE, FAKE, float("nan"), FAKE, stream=0)
+    assert e.value.status == D.ERR_INVALID_ARG
