@@ -336,6 +336,84 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* tb, uint32_t valid,
   }
 }
 
+// attend_chunk for the shapes whose rows are gathered one wave instruction
+// per row (Dv = 512), with part of the softmax hidden behind the PV MFMAs.
+// Counters of attend_chunk: the matrix cores were busy 41% of the kernel and
+// co-issued with the VALU in only 1.3% of cycles, since QK, softmax and PV
+// ran one after the other.  Here the PV product runs K step 0 (rows 0..15:
+// weights 0..7 of each lane) over all 16 dim tiles, then K step 1; the
+// weights of K step 1 are computed in the gaps of the first 8 MFMAs of step
+// 0.  Each gap's work stays where it is placed (sched_barrier), so the V^T
+// operand loads keep their short lookahead.  Every accumulator and the
+// softmax sum see the same operations in the same order as in attend_chunk,
+// so the results are the same bits.
+template <int DK, int DV, int NW>
+__device__ __forceinline__ void attend_chunk_ov(const uint16_t* tb, uint32_t valid, const v8bf (&qb)[DK / 16],
+                                                float zscale, RowState<DK, DV, NW>& rs) {
+  using C = Cfg<DK, DV, NW>;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const v16f st = qk_chunk<DK, DV, NW>(tb, qb);
+  float z[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) z[j] = st[j];
+  if (valid != 0xFFFFFFFFu) {   // wave-uniform
+    const uint32_t vh = valid >> (4 * half);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + (j & 3);
+      if (!((vh >> r) & 1u)) z[j] = -INFINITY;
+    }
+  }
+  float mx = z[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, z[j]);
+  mx = max_halves(mx) * zscale;
+  if (rs.m_ref == -INFINITY) rs.m_ref = mx;
+  rs.m_seen = fmaxf(rs.m_seen, mx);
+  const float nref = -rs.m_ref;
+  v8bf pb[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(z[j], zscale, nref));
+    rs.l_sum += pj;
+    pb[0][j] = (__bf16)pj;
+  }
+  const int g = lane >> 4, jl = lane & 15;
+  const int vrow = 4 * (g >> 1) + (jl >> 2);
+  const int vpiece = 2 * (g & 1) + ((jl & 3) >> 1);
+  const int vsub = 4 * (jl & 1);
+  const uint16_t* v_lo = tb + (vrow * C::kRA + (vpiece ^ swz_a(vrow))) * 8 + vsub;
+  const uint16_t* v_hi = tb + ((vrow + 8) * C::kRA + (vpiece ^ swz_a(vrow + 8))) * 8 + vsub;
+  // MFMA n: K step kk = n / kNT over dim tile t = n % kNT
+  auto load_v = [&](int n) {
+    const int kk = n / C::kNT, t = n % C::kNT;
+    const int off = 16 * kk * C::kRA * 8 + 32 * t;
+    const v4bf lo = lds_read_tr16(v_lo + off);
+    const v4bf hi = lds_read_tr16(v_hi + off);
+    return (v8bf)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  constexpr int kM = 2 * C::kNT;
+  v8bf vbuf[kLookV];
+#pragma unroll
+  for (int j = 0; j < kLookV; ++j) vbuf[j] = load_v(j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < kM; ++n) {
+    const v8bf cur = vbuf[n % kLookV];
+    if (n + kLookV < kM) vbuf[n % kLookV] = load_v(n + kLookV);
+    const int kk = n / C::kNT, t = n % C::kNT;
+    rs.o[t] = mfma_bf16_32x32x16(cur, pb[kk], rs.o[t]);
+    if (n < 8) {
+      const int j = 8 + n;
+      const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(z[j], zscale, nref));
+      rs.l_sum += pj;
+      pb[1][j - 8] = (__bf16)pj;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int DK, int DV, int NW, bool kPaged>
 __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   using C = Cfg<DK, DV, NW>;
@@ -443,9 +521,14 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
     // refilled next was last read (and consumed) in chunk c-1.
     if (c + 1 < nchunks) wait_vm<ndma>(); else wait_vm<0>();
     asm volatile("s_barrier" ::: "memory");
-    if (c + 2 < nchunks) gather(c + 2, fill, ra, rb);
     const uint32_t valid = (uint32_t)__builtin_amdgcn_ballot_w64(lane < kChunk && rv >= 0);
-    if (valid != 0u) attend_chunk<DK, DV, NW>(cur, valid, qb, zscale, rs);
+    if constexpr (C::kRowDma) {
+      if (c + 2 < nchunks) gather(c + 2, fill, ra, rb);
+      if (valid != 0u) attend_chunk_ov<DK, DV, NW>(cur, valid, qb, zscale, rs);
+    } else {
+      if (c + 2 < nchunks) gather(c + 2, fill, ra, rb);
+      if (valid != 0u) attend_chunk<DK, DV, NW>(cur, valid, qb, zscale, rs);
+    }
   };
 
   for (int pass = 0; pass < 2; ++pass) {
