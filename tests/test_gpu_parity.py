@@ -410,6 +410,57 @@ def test_forward_bitwise_equals_chained_calls(name):
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
+def chained_forward(wl, d):
+    """dsa_indexer_scores, dsa_topk and dsa_sparse_mla_attn one after the other."""
+    dims = dsa.Dims.of(wl)
+    sc = run_indexer(wl, d)
+    idx_c = torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(dims, sc, wl.n_kv, idx_c)
+    del sc
+    out_c = torch.empty((wl.batch, wl.n_q, wl.heads, wl.dim_v), dtype=torch.int16, device="cuda")
+    lse_c = torch.empty((wl.batch, wl.n_q, wl.heads), dtype=torch.float32, device="cuda")
+    nws = dsa.dsa_attn_workspace_size(dims)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_attn(dims, d["q"], d["kv"], idx_c, wl.sm_scale, out_c, lse_c, ws, nws)
+    torch.cuda.synchronize()
+    return out_c, lse_c, idx_c
+
+
+def assert_forward_equals_chained(wl, d):
+    out, lse, idx = run_forward(wl, d)
+    out_c, lse_c, idx_c = chained_forward(wl, d)
+    assert torch.equal(idx, idx_c)
+    assert torch.equal(out, out_c)
+    assert torch.equal(lse.view(torch.int32), lse_c.view(torch.int32))
+    return idx
+
+
+def test_forward_all_scores_equal():
+    """Every key identical: all of a row's 64,000+ scores are equal, the
+    sampled cutoff collects every key (far more than the candidate list
+    holds) and each row takes the two-pass fallback.  Still the chained
+    result, and the ties go to the lowest indices (analysis page, Sec. 5.2:
+    equal scores at the cutoff are legitimate)."""
+    wl = INDEXER_CASES["two_chunks"]
+    d = SD.fill_inputs(wl)
+    d["k_idx"].fill_(0x38)     # e4m3 1.0
+    d["k_scale"].fill_(1.0)
+    idx = assert_forward_equals_chained(wl, d)
+    want = torch.arange(wl.topk, dtype=torch.int32, device="cuda").expand(wl.batch, wl.n_q, wl.topk)
+    assert torch.equal(idx, want)
+
+
+def test_forward_long_prefill_from_position_zero():
+    """A 20480-token prefill from position 0 in chunks of 3264 rows: short
+    and long rows, a ragged last chunk; the whole result is the chained
+    one."""
+    wl = W.custom("p4k", n_q=20480, n_kv=20480, q_pos0=0)
+    plan = dsa.dsa.dsa_forward_plan_of(dsa.Dims.of(wl))
+    assert plan.chunk_rows == 3264 and wl.n_q % plan.chunk_rows != 0
+    d = SD.fill_inputs(wl)
+    assert_forward_equals_chained(wl, d)
+
+
 def test_forward_ordered_on_caller_stream():
     """Rows spanning several chunks all run on the caller's stream.  Work
     enqueued on that stream just before the call (the query copy) must be
