@@ -754,12 +754,14 @@ int lds_slots() {
 // keys, measured) plus one step per 32 keys, and the launch runs in rounds
 // of `slots` workgroups; dispatch takes full key blocks first and each
 // query block's shorter last block at the end.  The length (a multiple of
-// the 256-key sub-block, up to 8192) minimises an estimate of the
+// the 256-key sub-block, up to 16384) minimises an estimate of the
 // makespan: whole rounds of full blocks, a last partial round, and the
 // short blocks, which after whole rounds mostly start in the slots freed
 // by the earliest finishers (kAbsorb: the share of their length that
-// still shows).  On 256-row chunks of a 128K prefill this picks the
-// fastest of the lengths measured at every position tried.  The estimate
+// still shows).  On 256-row chunks of a 128K prefill this picked the
+// fastest of the lengths measured at every position tried; on 512-row
+// chunks, allowing 16384 instead of 8192 took a whole 128K indexer pass
+// from 56.8 to 56.1 ms (32768 gained nothing more).  The estimate
 // assumes query blocks of about equal extent; spans whose extents differ
 // by 2048 keys or more (a whole causal triangle) return 0, and the caller
 // falls back to its default.  Scores do not depend on it.
@@ -772,7 +774,7 @@ int lds_keys_per_wg(const IndexerArgs& a, int nqb, int slots) {
   }
   double best_t = 1e300;
   int best = 2048;
-  for (int kpw = 256; kpw <= 8192; kpw += 256) {
+  for (int kpw = 256; kpw <= 16384; kpw += 256) {
     int64_t nfull = 0, npart = 0;
     int dpart = 0;
     for (int qb = 0; qb < nqb; ++qb) {
