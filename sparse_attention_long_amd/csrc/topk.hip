@@ -4,37 +4,40 @@
 // the cutoff are legitimate, Sec. 5.2 near Eq. (18) -- here they go to the
 // lower index).
 //
-// One workgroup of 1024 threads per row.  Scores are mapped to
-// order-preserving 32-bit keys (NaN lowest, -0 == +0); tau, the m-th largest
-// key, is found as follows.
+// One workgroup of 512 threads per row.  Scores are mapped to
+// order-preserving 32-bit keys (NaN lowest, -0 == +0).  The selection is
+// fixed by tau, the m-th largest key, and `need`, the number of keys equal
+// to tau that are kept (the lowest-indexed ones):
 //   Sampled single pass (the usual path): 2048 scores (32 blocks of 64
 //          spread over the row) give a provisional cutoff lo, the lower
 //          edge of the 13-bit bin (sign, exponent, 4 mantissa bits) that
 //          holds the sample's rank-r key, with r set so that about 2m keys
 //          of the row are expected at or above lo.  One pass over the row
-//          appends every key >= lo, with its index, to an LDS candidate list
-//          (one LDS atomic per wave per iteration; ballots give the slots).
-//          If between m and `cap` keys were collected, tau is among them:
-//          its 13-bit bin, then the 10- and 9-bit digits, are resolved on
-//          the candidates in LDS.
-//   Fallback (the sample missed): pass 1 builds the LDS histogram of the
-//          13-bit digit over the whole row and fixes tau's bin b1; pass 2
-//          marks the keys above b1 and collects bin b1 into the candidate
-//          list; a bin wider than the list takes one more pass per digit.
-// Keys above tau go into a selection bitmap and keys equal to tau into a
-// tie bitmap; the first (m - #above) ties in index order are kept, and the
-// bitmap is emitted in ascending order with a block-wide popcount prefix
-// sum.  The selection needs no sort.
-//
-// The row is streamed with 16-byte loads, four per thread in flight (64 KB
-// per workgroup), after a scalar head that reaches 16-byte alignment.
+//          collects every key >= lo, with its index, into an LDS candidate
+//          list in ascending index order: in each iteration a thread takes
+//          16 consecutive scores, and one block-wide prefix sum of the
+//          threads' counts places their candidates.  If between m and kCap
+//          keys were collected, tau and need come from a radix select over
+//          the candidates.
+//   Fallback (the sample missed): pass 1 builds the histogram of the 13-bit
+//          digit over the whole row and fixes tau's bin b1.  If the keys at
+//          or above b1 fit the list, pass 2 collects them (in order) and
+//          the selection proceeds as above; a wider bin takes one more pass
+//          per remaining digit to fix tau and need, and a last ordered pass
+//          writes the selection.
+// Because the candidates are in index order, the selection is written by an
+// order-keeping compaction (every key above tau, then the first `need` keys
+// equal to tau, in index order) with no bitmap and no sort.  The 13-bit
+// histogram and the candidate list share their LDS, so a row needs about
+// 70 KB and two rows run on a CU at once (512 threads each, at most 128
+// VGPRs): one row's serial phases overlap the other's streaming.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxKV = 262144;
 constexpr int kShift1 = 19;                 // digit 1 = key bits 31..19
@@ -42,9 +45,10 @@ constexpr int kBins1 = 1 << (32 - kShift1); // 8192
 constexpr int kShift2 = 9;                  // digit 2 = key bits 18..9
 constexpr int kBins2 = 1 << (kShift1 - kShift2);   // 1024
 constexpr int kBins3 = 1 << kShift2;        // digit 3 = key bits 8..0: 512
-constexpr int kMaxCand = 8192;
-constexpr int kDynLds = 163840 - 1024;      // dynamic LDS bytes (the rest: static)
-constexpr int kUnroll = 4;                  // 16-byte loads in flight per thread
+constexpr int kCap = 8192;                  // candidates of a row in LDS
+constexpr int kSlice = kCap / kThreads;     // candidates per thread in the selection
+constexpr int kVec = 4;                     // float4s per thread and iteration: 16 consecutive scores
+constexpr int kCapPart = 4096;              // candidates per part of the split top-k
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -55,11 +59,28 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 struct Shared {
   uint32_t scan[kWaves];
-  uint32_t bin, above, ncand;
+  uint32_t bin, above, total, flag;
 };
 
-// Exclusive prefix sum over the block in thread order.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh) {
+// LDS of a row's workgroup.  The 13-bit histogram (cutoff search, fallback
+// pass 1) and the candidate list are never needed at the same time.
+template <int CAP>
+struct RowLds {
+  union {
+    uint32_t hist1[kBins1];
+    struct {
+      uint32_t key[CAP];
+      uint32_t idx[CAP];
+    } c;
+  } u;
+  uint32_t hist2[kBins2];   // digits 2 and 3, the 8-bit digits, reductions
+  Shared sh;
+};
+static_assert(2 * kCap >= kBins1 && 2 * kCapPart >= kBins1, "the histogram fits the candidate space");
+static_assert(2048 % kThreads == 0 && kThreads >= 256 && kCap % kThreads == 0, "sample and slice shapes");
+
+// Exclusive prefix sum over the block in thread order, and the block total.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, Shared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -69,9 +90,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh)
   }
   if (lane == 63) sh.scan[wave] = x;
   __syncthreads();
-  uint32_t pre = 0;
-  for (int w = 0; w < wave; ++w) pre += sh.scan[w];
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t s = sh.scan[w];
+    pre += w < wave ? s : 0u;
+    tot += s;
+  }
   __syncthreads();
+  total = tot;
   return pre + x - v;
 }
 
@@ -85,7 +112,8 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t rank, Shared&
   uint32_t local = 0;
   for (int j = 0; j < per; ++j)
     if (top - j >= 0) local += hist[top - j];
-  const uint32_t excl = block_exclusive_scan(local, sh);
+  uint32_t tot;
+  const uint32_t excl = block_scan(local, tot, sh);
   if (local > 0 && excl < rank && rank <= excl + local) {
     uint32_t cum = excl;
     for (int j = 0; j < per && top - j >= 0; ++j) {
@@ -95,48 +123,6 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t rank, Shared&
     }
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ void set_bit(uint32_t* bm, int e) { atomicOr(&bm[e >> 5], 1u << (e & 31)); }
-
-// Keep only the lowest `keep` set bits of w.
-__device__ __forceinline__ uint32_t keep_lowest(uint32_t w, uint32_t keep) {
-  uint32_t r = 0;
-  while (keep-- > 0 && w) { const uint32_t low = w & (0u - w); r |= low; w ^= low; }
-  return r;
-}
-
-// Append (key, e) for the lanes with c set: one LDS atomic per wave.  Must be
-// reached by whole waves (wave-uniform control flow).
-__device__ __forceinline__ void append_wave(bool c, uint32_t key, uint32_t e, uint32_t* ckey, uint32_t* cidx,
-                                            int cap, Shared& sh) {
-  const uint64_t m = __ballot(c);
-  if (m == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)m) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(m));
-  base = __shfl(base, leader, 64);
-  if (c) {
-    const uint64_t below = lane == 0 ? 0ull : (m & (~0ull >> (64 - lane)));
-    const uint32_t pos = base + (uint32_t)__popcll(below);
-    if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = e; }
-  }
-}
-
-// Exclusive prefix over the wave of per-lane counts below 32, and the
-// wave total, from five ballots (no LDS traffic).
-__device__ __forceinline__ uint32_t wave_prefix_small(uint32_t cnt, uint32_t& total) {
-  uint32_t pre = 0;
-  total = 0;
-#pragma unroll
-  for (int bit = 0; bit < 5; ++bit) {
-    const uint64_t bm = __ballot((cnt >> bit) & 1u);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-    pre += below << bit;
-    total += (uint32_t)__popcll(bm) << bit;
-  }
-  return pre;
 }
 
 // The row split for vector loads: elements [0, h) are read one by one
@@ -154,139 +140,334 @@ struct RowSplit {
   }
 };
 
-// Calls f(e, key, valid) for every element of the row.  The vector part runs
-// the same number of iterations in every thread (block-uniform), so f may
-// use wave-wide operations; elements past the end come with valid = false.
-// The < 8 head and tail elements are visited by threads 0..7 afterwards with
-// a per-thread (not wave-uniform) call g(e, key).
+// Calls f(key, valid) for every element of the row, in no particular order
+// (histogram passes): 16-byte loads, consecutive lanes on consecutive
+// float4s, four per thread in flight.  The vector part runs the same number
+// of iterations in every thread (block-uniform), so f may use wave-wide
+// operations.  The < 8 head and tail elements are visited by threads 0..7
+// afterwards with a per-thread call g(key).
 template <class F, class G>
 __device__ __forceinline__ void scan_row(const RowSplit& r, F&& f, G&& g) {
   const int t = threadIdx.x;
-  const int iters = (r.nq + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  const int iters = (r.nq + kThreads * kVec - 1) / (kThreads * kVec);
   for (int it = 0; it < iters; ++it) {
-    float4 v[kUnroll];
-    bool ok[kUnroll];
+    float4 v[kVec];
+    bool ok[kVec];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int q = (it * kUnroll + u) * kThreads + t;
+    for (int u = 0; u < kVec; ++u) {
+      const int q = (it * kVec + u) * kThreads + t;
       ok[u] = q < r.nq;
       v[u] = r.xv[ok[u] ? q : 0];
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = r.h + 4 * ((it * kUnroll + u) * kThreads + t);
-      f(e + 0, order_key(v[u].x), ok[u]);
-      f(e + 1, order_key(v[u].y), ok[u]);
-      f(e + 2, order_key(v[u].z), ok[u]);
-      f(e + 3, order_key(v[u].w), ok[u]);
+    for (int u = 0; u < kVec; ++u) {
+      f(order_key(v[u].x), ok[u]);
+      f(order_key(v[u].y), ok[u]);
+      f(order_key(v[u].z), ok[u]);
+      f(order_key(v[u].w), ok[u]);
     }
   }
-  if (t < r.h) g(t, order_key(r.x[t]));
-  if (t >= 4 && t - 4 < r.n - r.tail0) g(r.tail0 + t - 4, order_key(r.x[r.tail0 + t - 4]));
+  if (t < r.h) g(order_key(r.x[t]));
+  if (t >= 4 && t - 4 < r.n - r.tail0) g(order_key(r.x[r.tail0 + t - 4]));
 }
 
-// Candidates of a row collected by the parts of topk_collect_kernel.
+// The ordered passes: iteration it of a range of float4s starting at q0
+// gives thread t the float4s q0 + (it * kThreads + t) * kVec + u, u < kVec:
+// 16 consecutive scores, so that thread order is element order.  Loads v
+// and the keys of the thread's scores (valid: inside [q0, q1)).
+__device__ __forceinline__ int ordered_keys(const RowSplit& r, int q0, int q1, int it, uint32_t (&keys)[4 * kVec],
+                                            uint32_t& valid) {
+  const int qb = q0 + (it * kThreads + (int)threadIdx.x) * kVec;
+  float4 v[kVec];
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) v[u] = r.xv[qb + u < q1 ? qb + u : q0];
+  valid = 0;
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    keys[4 * u + 0] = order_key(v[u].x);
+    keys[4 * u + 1] = order_key(v[u].y);
+    keys[4 * u + 2] = order_key(v[u].z);
+    keys[4 * u + 3] = order_key(v[u].w);
+    valid |= (qb + u < q1 ? 0xFu : 0u) << (4 * u);
+  }
+  return r.h + 4 * qb;   // element index of keys[0]
+}
+
+// Appends, in ascending element order, every element of the float4 range
+// [q0, q1) whose key is >= lo -- preceded by those of the scalar head
+// elements [0, h) if `head` and followed by those of the tail elements
+// [tail0, n) if `tail` -- to the candidate list (key, idx), counting also
+// past `cap` but storing only below it.  Returns the count (block-uniform).
+__device__ uint32_t collect_ordered(const RowSplit& r, int q0, int q1, bool head, bool tail, uint32_t lo,
+                                    uint32_t* ckey, uint32_t* cidx, uint32_t cap, Shared& sh) {
+  const int t = threadIdx.x;
+  uint32_t base = 0;
+  if (head && r.h > 0) {
+    if (t == 0) {
+      uint32_t c = 0;
+      for (int e = 0; e < r.h; ++e) {
+        const uint32_t key = order_key(r.x[e]);
+        if (key >= lo) {
+          if (c < cap) { ckey[c] = key; cidx[c] = (uint32_t)e; }
+          ++c;
+        }
+      }
+      sh.total = c;
+    }
+    __syncthreads();
+    base = sh.total;
+    __syncthreads();
+  }
+  const int iters = (q1 - q0 + kThreads * kVec - 1) / (kThreads * kVec);
+  for (int it = 0; it < iters; ++it) {
+    uint32_t keys[4 * kVec], valid;
+    const int e0 = ordered_keys(r, q0, q1, it, keys, valid);
+    uint32_t cm = 0;
+#pragma unroll
+    for (int j = 0; j < 4 * kVec; ++j) cm |= (keys[j] >= lo ? 1u : 0u) << j;
+    cm &= valid;
+    uint32_t tot;
+    uint32_t pos = base + block_scan((uint32_t)__popc(cm), tot, sh);
+#pragma unroll
+    for (int j = 0; j < 4 * kVec; ++j)
+      if ((cm >> j) & 1u) {
+        if (pos < cap) { ckey[pos] = keys[j]; cidx[pos] = (uint32_t)(e0 + j); }
+        ++pos;
+      }
+    base += tot;
+  }
+  if (tail && r.tail0 < r.n) {
+    if (t == 0) {
+      uint32_t c = base;
+      for (int e = r.tail0; e < r.n; ++e) {
+        const uint32_t key = order_key(r.x[e]);
+        if (key >= lo) {
+          if (c < cap) { ckey[c] = key; cidx[c] = (uint32_t)e; }
+          ++c;
+        }
+      }
+      sh.total = c;
+    }
+    __syncthreads();
+    base = sh.total;
+    __syncthreads();
+  }
+  return base;
+}
+
+// A thread's slice of the candidate list, in registers: entries
+// [t * per, t * per + n) with per = ceil(nc / kThreads) <= kSlice.
+struct Slice {
+  uint32_t key[kSlice], idx[kSlice];
+  uint32_t n;
+};
+
+__device__ __forceinline__ void load_slice(const uint32_t* ckey, const uint32_t* cidx, uint32_t nc, Slice& s) {
+  const uint32_t per = (nc + kThreads - 1) / kThreads;
+  const uint32_t j0 = min((uint32_t)threadIdx.x * per, nc);
+  s.n = min(j0 + per, nc) - j0;
+#pragma unroll
+  for (int u = 0; u < kSlice; ++u) {
+    const bool ok = (uint32_t)u < s.n;
+    s.key[u] = ok ? ckey[j0 + u] : 0u;
+    s.idx[u] = ok ? cidx[j0 + u] : 0u;
+  }
+}
+
+// tau, the m-th largest key of the candidates held in the threads' slices
+// (m <= their number), and need, how many keys equal to tau are selected.
+// The bits every candidate shares (above the highest bit where the largest
+// and smallest keys differ) are fixed at once; the rest are resolved 8 at
+// a time from the top, with a 256-bin histogram in `hist`.
+__device__ void select_tau(const Slice& s, uint32_t m, uint32_t* hist, Shared& sh, uint32_t& tau, uint32_t& need) {
+  const int t = threadIdx.x;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int u = 0; u < kSlice; ++u)
+    if ((uint32_t)u < s.n) {
+      kmax = max(kmax, s.key[u]);
+      kmin = min(kmin, s.key[u]);
+    }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, kWave));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, kWave));
+  }
+  if ((t & 63) == 0) {
+    hist[t >> 6] = kmax;
+    hist[kWaves + (t >> 6)] = kmin;
+  }
+  __syncthreads();
+  kmax = 0u;
+  kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    kmax = max(kmax, hist[w]);
+    kmin = min(kmin, hist[kWaves + w]);
+  }
+  __syncthreads();
+  int hi = kmax == kmin ? -1 : 31 - __clz(kmax ^ kmin);   // highest differing bit
+  uint32_t pmask = hi < 0 ? 0xFFFFFFFFu : hi >= 31 ? 0u : ~((2u << hi) - 1u);
+  uint32_t prefix = kmax & pmask, rank = m;
+  while (hi >= 0) {   // block-uniform
+    const int lo_bit = max(hi - 7, 0);
+    const uint32_t dmask = (2u << (hi - lo_bit)) - 1u;
+    if (t < 256) hist[t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSlice; ++u)
+      if ((uint32_t)u < s.n && (s.key[u] & pmask) == prefix) atomicAdd(&hist[(s.key[u] >> lo_bit) & dmask], 1u);
+    __syncthreads();
+    const uint32_t c = t < 256 ? hist[255 - t] : 0u;   // thread t < 256 owns bin 255 - t
+    uint32_t tot;
+    const uint32_t above = block_scan(c, tot, sh);
+    if (c > 0 && above < rank && rank <= above + c) {
+      sh.bin = (uint32_t)(255 - t);
+      sh.above = above;
+    }
+    __syncthreads();
+    prefix |= sh.bin << lo_bit;
+    pmask |= dmask << lo_bit;
+    rank -= sh.above;
+    hi = lo_bit - 1;
+    __syncthreads();
+  }
+  tau = prefix;
+  need = rank;
+}
+
+// Writes the selection from the slices (which are in element order): every
+// key above tau and the first `need` keys equal to tau, in element order.
+__device__ void emit_slices(const Slice& s, uint32_t tau, uint32_t need, uint32_t m, int32_t* out, Shared& sh) {
+  uint32_t ties = 0;
+#pragma unroll
+  for (int u = 0; u < kSlice; ++u) ties += (uint32_t)u < s.n && s.key[u] == tau ? 1u : 0u;
+  uint32_t tot;
+  const uint32_t tie0 = block_scan(ties, tot, sh);
+  uint32_t keep = 0;
+  {
+    uint32_t tr = tie0;
+#pragma unroll
+    for (int u = 0; u < kSlice; ++u) {
+      if ((uint32_t)u >= s.n) continue;
+      if (s.key[u] > tau) ++keep;
+      else if (s.key[u] == tau) keep += tr++ < need ? 1u : 0u;
+    }
+  }
+  uint32_t pos = block_scan(keep, tot, sh);
+  uint32_t tr = tie0;
+#pragma unroll
+  for (int u = 0; u < kSlice; ++u) {
+    if ((uint32_t)u >= s.n) continue;
+    const bool k = s.key[u] > tau || (s.key[u] == tau && tr++ < need);
+    if (k && pos < m) out[pos++] = (int32_t)s.idx[u];
+  }
+}
+
+// The last pass of the wide-bin fallback: writes, in element order, every
+// element whose key is above tau and the first `need` with key tau.
+__device__ void write_selection(const RowSplit& r, uint32_t tau, uint32_t need, uint32_t m, int32_t* out,
+                                Shared& sh) {
+  const int t = threadIdx.x;
+  uint32_t base = 0, tbase = 0;   // selected and ties so far (block-uniform)
+  auto serial = [&](int e0, int e1) {   // thread 0 only
+    for (int e = e0; e < e1; ++e) {
+      const uint32_t key = order_key(r.x[e]);
+      if (key > tau || (key == tau && tbase++ < need)) {
+        if (base < m) out[base] = e;
+        ++base;
+      }
+    }
+  };
+  if (r.h > 0) {
+    if (t == 0) {
+      serial(0, r.h);
+      sh.bin = base;
+      sh.above = tbase;
+    }
+    __syncthreads();
+    base = sh.bin;
+    tbase = sh.above;
+    __syncthreads();
+  }
+  const int iters = (r.nq + kThreads * kVec - 1) / (kThreads * kVec);
+  for (int it = 0; it < iters; ++it) {
+    uint32_t keys[4 * kVec], valid;
+    const int e0 = ordered_keys(r, 0, r.nq, it, keys, valid);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < 4 * kVec; ++j) {
+      gt |= (keys[j] > tau ? 1u : 0u) << j;
+      eq |= (keys[j] == tau ? 1u : 0u) << j;
+    }
+    gt &= valid;
+    eq &= valid;
+    uint32_t ttot;
+    const uint32_t tpre = tbase + block_scan((uint32_t)__popc(eq), ttot, sh);
+    // this thread's kept ties: those whose rank tpre + (ties before) < need
+    uint32_t keepm = gt, tr = tpre;
+#pragma unroll
+    for (int j = 0; j < 4 * kVec; ++j)
+      if ((eq >> j) & 1u) keepm |= (tr++ < need ? 1u : 0u) << j;
+    uint32_t ktot;
+    uint32_t pos = base + block_scan((uint32_t)__popc(keepm), ktot, sh);
+#pragma unroll
+    for (int j = 0; j < 4 * kVec; ++j)
+      if ((keepm >> j) & 1u) {
+        if (pos < m) out[pos] = e0 + j;
+        ++pos;
+      }
+    base += ktot;
+    tbase += ttot;
+  }
+  if (r.tail0 < r.n && t == 0) serial(r.tail0, r.n);
+  __syncthreads();
+}
+
+// Sampled cutoff of a row: 32 blocks of 64 scores spread over the row give
+// a conservative lower bound lo for tau (the sample's rank-r 13-bit bin, r
+// chosen so that about 2m keys are expected at or above it).  hist (kBins1)
+// must be zero on entry.  A row of fewer than 64 scores has no room for the
+// sample blocks: its cutoff is 0, the lowest key, so every score becomes a
+// candidate (n < 64 fits any candidate list).  n is block-uniform, so the
+// early return keeps the barriers uniform.
+// Sample indices: block blk starts at floor(blk (n - 64) / 31) in [0, n - 64]
+// and its 64 scores end at most at n - 1.
+__device__ __forceinline__ uint32_t sampled_cutoff(const RowSplit& row, int n, int m, uint32_t* hist, Shared& sh) {
+  if (n < 64) return 0u;
+  constexpr int kPer = 2048 / kThreads;   // sample scores per thread
+  constexpr int kTpb = 64 / kPer;         // threads per block of 64
+  const int t = threadIdx.x;
+  const int blk = t / kTpb;
+  const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + kPer * (t % kTpb);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) atomicAdd(&hist[order_key(row.x[e0 + j]) >> kShift1], 1u);
+  __syncthreads();
+  const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
+  find_bin(hist, kBins1, r, sh);
+  return sh.bin << kShift1;
+}
+
+__device__ __forceinline__ void zero(uint32_t* p, int n) {
+  for (int j = threadIdx.x; j < n; j += kThreads) p[j] = 0u;
+}
+
+// Candidates of a row collected by the parts of topk_collect_kernel, each
+// part's list in element order and the parts in row order.
 struct Parts {
   uint32_t* cnt;   // [rows_total * nparts] keys each part found at or above its cutoff
   uint32_t* key;   // [rows_total * nparts * kCapPart]
   uint32_t* idx;
   int nparts;
 };
-constexpr int kCapPart = 4096;   // candidates kept per part
-
-// Sampled cutoff of a row: 32 blocks of 64 scores spread over the row give
-// a conservative lower bound lo for tau (the sample's rank-r 13-bit bin, r
-// chosen so that about 2m keys are expected at or above it).  hist (kBins1,
-// zero on entry) is zero again on return.  A row of fewer than 64 scores has
-// no room for the sample blocks: its cutoff is 0, the lowest key, so every
-// score becomes a candidate (n < 64 fits any candidate list).  n is
-// block-uniform, so the early return keeps the barriers uniform.
-// Sample indices: block blk starts at floor(blk (n - 64) / 31) in [0, n - 64]
-// and its 64 scores end at most at n - 1.
-__device__ __forceinline__ uint32_t sampled_cutoff(const RowSplit& row, int n, int m, uint32_t* hist, Shared& sh) {
-  if (n < 64) return 0u;
-  const int t = threadIdx.x;
-  const int blk = t >> 5;
-  const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + 2 * (t & 31);
-  atomicAdd(&hist[order_key(row.x[e0]) >> kShift1], 1u);
-  atomicAdd(&hist[order_key(row.x[e0 + 1]) >> kShift1], 1u);
-  __syncthreads();
-  const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
-  find_bin(hist, kBins1, r, sh);
-  const uint32_t lo = sh.bin << kShift1;
-  for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
-  return lo;
-}
-
-// Appends every key >= lo of the row's vector elements [q0, q1) (float4
-// units), plus the scalar head (head) and tail (tail) elements, with its
-// index, to the LDS candidate list (sh.ncand counts all of them, also past
-// cap).  One wave-level append per iteration: each lane marks its
-// candidates among its 4 x 4 scores, the wave forms the prefix of the
-// counts from ballots, and one LDS atomic reserves the wave's slots.
-__device__ __forceinline__ void collect_range(const RowSplit& row, int q0, int q1, bool head, bool tail_part,
-                                              uint32_t lo, uint32_t* ckey, uint32_t* cidx, int cap, Shared& sh) {
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int iters = (q1 - q0 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-  for (int it = 0; it < iters; ++it) {
-    float4 v[kUnroll];
-    bool ok[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int q = q0 + (it * kUnroll + u) * kThreads + t;
-      ok[u] = q < q1;
-      v[u] = row.xv[ok[u] ? q : 0];
-    }
-    uint32_t keys[4 * kUnroll];
-    uint32_t cm = 0;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      keys[4 * u + 0] = order_key(v[u].x);
-      keys[4 * u + 1] = order_key(v[u].y);
-      keys[4 * u + 2] = order_key(v[u].z);
-      keys[4 * u + 3] = order_key(v[u].w);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) cm |= (ok[u] && keys[4 * u + c] >= lo ? 1u : 0u) << (4 * u + c);
-    }
-    uint32_t total;
-    const uint32_t pre = wave_prefix_small((uint32_t)__popc(cm), total);
-    if (total != 0) {   // wave-uniform
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&sh.ncand, total);
-      base = __shfl(base, 0, 64);
-      uint32_t pos = base + pre;
-#pragma unroll
-      for (int j = 0; j < 4 * kUnroll; ++j) {
-        if ((cm >> j) & 1u) {
-          if (pos < (uint32_t)cap) {
-            ckey[pos] = keys[j];
-            cidx[pos] = (uint32_t)(row.h + 4 * (q0 + (it * kUnroll + (j >> 2)) * kThreads + t) + (j & 3));
-          }
-          ++pos;
-        }
-      }
-    }
-  }
-  auto one = [&](int e) {
-    const uint32_t key = order_key(row.x[e]);
-    if (key >= lo) {
-      const uint32_t pos = atomicAdd(&sh.ncand, 1u);
-      if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
-    }
-  };
-  if (head && t < row.h) one(t);
-  if (tail_part && t >= 4 && t - 4 < row.n - row.tail0) one(row.tail0 + t - 4);
-}
 
 // Collection half of the split top-k: part f of a row (nparts per row, row
 // b * rows + i = blockIdx.x / nparts) takes the row's sampled cutoff (every
 // part computes the same one) and collects the keys at or above it among
-// its share of the row into the workspace.  Short rows (n <= k) write a
-// zero count; the merge kernel handles them.
+// its contiguous share of the row, in element order, into the workspace.
+// Short rows (n <= k) write a zero count; the merge kernel handles them.
 __global__ void __launch_bounds__(kThreads) topk_collect_kernel(TopkArgs a, Parts parts) {
-  extern __shared__ uint32_t lds[];
-  __shared__ Shared sh;
+  __shared__ RowLds<kCapPart> L;
   const int t = threadIdx.x;
   const int f = blockIdx.x % parts.nparts;
   const int rowid = blockIdx.x / parts.nparts;
@@ -299,246 +480,140 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(TopkArgs a, Part
     return;
   }
   const RowSplit row(a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld, n);
-  uint32_t* hist = lds;
-  uint32_t* ckey = hist + kBins1;
-  uint32_t* cidx = ckey + kCapPart;
-  for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
-  if (t == 0) sh.ncand = 0;
+  zero(L.u.hist1, kBins1);
   __syncthreads();
-  const uint32_t lo = sampled_cutoff(row, n, m, hist, sh);
+  const uint32_t lo = sampled_cutoff(row, n, m, L.u.hist1, L.sh);
   const int q0 = (int)((int64_t)row.nq * f / parts.nparts), q1 = (int)((int64_t)row.nq * (f + 1) / parts.nparts);
-  collect_range(row, q0, q1, f == 0, f == parts.nparts - 1, lo, ckey, cidx, kCapPart, sh);
+  const uint32_t nc = collect_ordered(row, q0, q1, f == 0, f == parts.nparts - 1, lo, L.u.c.key, L.u.c.idx,
+                                      kCapPart, L.sh);
   __syncthreads();
-  const uint32_t nc = sh.ncand;
   const int64_t base = ((int64_t)rowid * parts.nparts + f) * kCapPart;
   for (int j = t; j < (int)min(nc, (uint32_t)kCapPart); j += kThreads) {
-    parts.key[base + j] = ckey[j];
-    parts.idx[base + j] = cidx[j];
+    parts.key[base + j] = L.u.c.key[j];
+    parts.idx[base + j] = L.u.c.idx[j];
   }
   if (t == 0) *cnt = nc;
 }
 
 // The selection of one row (blockIdx.x = b * rows + i).  kParts: the
-// candidates come from topk_collect_kernel's parts when they are usable
-// (no part overflowed and m <= total <= cap), else the row takes the
-// two-pass fallback; otherwise the row is sampled and collected here.
+// candidates come from topk_collect_kernel's parts when they are usable (no
+// part overflowed and m <= total <= kCap); otherwise, and without parts,
+// the row is sampled and collected here, with the two-pass fallback.
 template <bool kParts>
-__device__ __forceinline__ void topk_row(const TopkArgs& a, int cap, const Parts& parts) {
-  extern __shared__ uint32_t lds[];
-  __shared__ Shared sh;
+__device__ __forceinline__ void topk_row(const TopkArgs& a, const Parts& parts) {
+  __shared__ RowLds<kCap> L;
   const int t = threadIdx.x;
   const int b = blockIdx.x / a.rows;
   const int i = blockIdx.x % a.rows;
   const int n = min(row_pos_base(a.pk, b, a.S, a.pos0) + i + 1, a.S);
-  const int m = min(a.k, n);
+  const uint32_t m = (uint32_t)min(a.k, n);
   int32_t* out = a.idx + ((int64_t)b * a.idx_rows_b + i) * a.k;
   if (n <= a.k) {   // short row: every candidate is selected
     for (int j = t; j < a.k; j += kThreads) out[j] = j < n ? j : -1;
     return;
   }
   const RowSplit row(a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld, n);
-  const int nwords = (n + 31) >> 5;
-  const int words_max = (a.S + 31) >> 5;
-  uint32_t* hist = lds;                  // kBins1 (reused for digits 2, 3)
-  uint32_t* selbm = hist + kBins1;       // nwords
-  uint32_t* tiebm = selbm + words_max;   // nwords
-  uint32_t* ckey = tiebm + words_max;    // cap
-  uint32_t* cidx = ckey + cap;           // cap
-
-  for (int j = t; j < kBins1; j += kThreads) hist[j] = 0;
-  for (int j = t; j < nwords; j += kThreads) { selbm[j] = 0; tiebm[j] = 0; }
-  if (t == 0) sh.ncand = 0;
-  __syncthreads();
-
-  // Digits 2 and 3 of tau among the candidate list (every key of bin b1 is
-  // on it; keys of other bins are filtered out), then the marks: keys above
-  // tau into the bitmap, keys equal to tau into the tie bitmap.
-  uint32_t tau, need;
-  auto select_candidates = [&](int nc, uint32_t b1, uint32_t rank1) {
-    for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
+  uint32_t* ckey = L.u.c.key;
+  uint32_t* cidx = L.u.c.idx;
+  uint32_t nc = 0;
+  bool have = false;   // block-uniform: [0, nc) of the list holds every key >= some cutoff, m <= nc <= kCap
+  if constexpr (kParts) {
+    // the parts' counts, one load per thread
+    if (t < parts.nparts) L.hist2[t] = parts.cnt[(int64_t)blockIdx.x * parts.nparts + t];
     __syncthreads();
-    for (int c = t; c < nc; c += kThreads)
-      if ((ckey[c] >> kShift1) == b1) atomicAdd(&hist[(ckey[c] >> kShift2) & (kBins2 - 1)], 1u);
-    __syncthreads();
-    find_bin(hist, kBins2, rank1, sh);
-    const uint32_t pre = (b1 << (kShift1 - kShift2)) | sh.bin;
-    const uint32_t rank2 = rank1 - sh.above;
-    for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
-    __syncthreads();
-    for (int c = t; c < nc; c += kThreads)
-      if ((ckey[c] >> kShift2) == pre) atomicAdd(&hist[ckey[c] & (kBins3 - 1)], 1u);
-    __syncthreads();
-    find_bin(hist, kBins3, rank2, sh);
-    tau = (pre << kShift2) | sh.bin;
-    need = rank2 - sh.above;
-    for (int c = t; c < nc; c += kThreads) {
-      const uint32_t key = ckey[c];
-      if (key > tau) set_bit(selbm, (int)cidx[c]);
-      else if (key == tau) set_bit(tiebm, (int)cidx[c]);
-    }
-  };
-
-  // ---- one pass with a sampled cutoff (or the parts' candidates): if
-  // between m and cap keys were collected, tau is the m-th largest candidate
-  // and the selection is exact; otherwise the two-pass radix select below
-  // runs.
-  bool done = false;
-  {
-    if constexpr (kParts) {
-      const int64_t pr = (int64_t)blockIdx.x * parts.nparts;
+    if (t == 0) {
       uint32_t tot = 0;
       bool over = false;
       for (int f = 0; f < parts.nparts; ++f) {
-        const uint32_t c = parts.cnt[pr + f];
-        tot += c;
+        const uint32_t c = L.hist2[f];
         over = over || c > (uint32_t)kCapPart;
+        L.hist2[kBins2 / 2 + f] = tot;   // the part's offset in the list
+        tot += c;
       }
-      const bool use = !over && tot >= (uint32_t)m && tot <= (uint32_t)cap;   // block-uniform
-      if (use) {
-        uint32_t off = 0;
-        for (int f = 0; f < parts.nparts; ++f) {
-          const uint32_t c = parts.cnt[pr + f];
-          const int64_t base = (pr + f) * kCapPart;
-          for (int j = t; j < (int)c; j += kThreads) {
-            ckey[off + j] = parts.key[base + j];
-            cidx[off + j] = parts.idx[base + j];
-          }
-          off += c;
+      L.sh.total = tot;
+      L.sh.flag = !over && tot >= m && tot <= (uint32_t)kCap ? 1u : 0u;
+    }
+    __syncthreads();
+    if (L.sh.flag) {
+      nc = L.sh.total;
+      for (int f = 0; f < parts.nparts; ++f) {
+        const uint32_t c = L.hist2[f], off = L.hist2[kBins2 / 2 + f];
+        const int64_t base = ((int64_t)blockIdx.x * parts.nparts + f) * kCapPart;
+        for (int j = t; j < (int)c; j += kThreads) {
+          ckey[off + j] = parts.key[base + j];
+          cidx[off + j] = parts.idx[base + j];
         }
       }
-      if (t == 0) sh.ncand = use ? tot : (uint32_t)cap + 1u;
-    } else {
-      const uint32_t lo = sampled_cutoff(row, n, m, hist, sh);
-      collect_range(row, 0, row.nq, true, true, lo, ckey, cidx, cap, sh);
+      have = true;
     }
     __syncthreads();
-    const uint32_t nc = sh.ncand;
-    if (nc >= (uint32_t)m && nc <= (uint32_t)cap) {   // block-uniform
-      for (int c = t; c < (int)nc; c += kThreads) atomicAdd(&hist[ckey[c] >> kShift1], 1u);
-      __syncthreads();
-      find_bin(hist, kBins1, (uint32_t)m, sh);
-      const uint32_t b1 = sh.bin;
-      const uint32_t rank1 = (uint32_t)m - sh.above;
-      select_candidates((int)nc, b1, rank1);
-      done = true;
-    } else {
-      if (t == 0) sh.ncand = 0;
-      __syncthreads();
-    }
   }
-
-  if (!done) {
-    // ---- pass 1: digit-1 histogram
-    scan_row(
-        row, [&](int, uint32_t key, bool ok) { if (ok) atomicAdd(&hist[key >> kShift1], 1u); },
-        [&](int, uint32_t key) { atomicAdd(&hist[key >> kShift1], 1u); });
+  if (!have) {
+    zero(L.u.hist1, kBins1);
     __syncthreads();
-    find_bin(hist, kBins1, (uint32_t)m, sh);
-    const uint32_t b1 = sh.bin;
-    const uint32_t rank1 = (uint32_t)m - sh.above;   // rank of tau inside bin b1
-    const uint32_t c1 = hist[b1];
+    const uint32_t lo = sampled_cutoff(row, n, (int)m, L.u.hist1, L.sh);
+    nc = collect_ordered(row, 0, row.nq, true, true, lo, ckey, cidx, kCap, L.sh);
+    have = nc >= m && nc <= (uint32_t)kCap;
+  }
+  if (!have) {
+    // ---- pass 1: digit-1 histogram over the row (the list is discarded)
     __syncthreads();
-    if (c1 <= (uint32_t)cap) {
-      // ---- pass 2: mark keys above bin b1, collect bin b1
+    zero(L.u.hist1, kBins1);
+    __syncthreads();
+    uint32_t* h1 = L.u.hist1;
+    scan_row(row, [&](uint32_t key, bool ok) { if (ok) atomicAdd(&h1[key >> kShift1], 1u); },
+             [&](uint32_t key) { atomicAdd(&h1[key >> kShift1], 1u); });
+    __syncthreads();
+    find_bin(h1, kBins1, m, L.sh);
+    const uint32_t b1 = L.sh.bin;
+    const uint32_t above1 = L.sh.above;
+    const uint32_t c1 = h1[b1];
+    __syncthreads();
+    if (above1 + c1 <= (uint32_t)kCap) {
+      // ---- pass 2: collect every key at or above bin b1, in order
+      nc = collect_ordered(row, 0, row.nq, true, true, b1 << kShift1, ckey, cidx, kCap, L.sh);
+      have = true;   // nc == above1 + c1, which lies in [m, kCap]
+    } else {
+      // ---- wide bin: digits 2 and 3 with one pass each, then the selection
+      uint32_t* h2 = L.hist2;
+      zero(h2, kBins2);
+      __syncthreads();
       scan_row(
-          row,
-          [&](int e, uint32_t key, bool ok) {
-            const uint32_t d = key >> kShift1;
-            if (ok && d > b1) set_bit(selbm, e);
-            append_wave(ok && d == b1, key, (uint32_t)e, ckey, cidx, cap, sh);
-          },
-          [&](int e, uint32_t key) {
-            const uint32_t d = key >> kShift1;
-            if (d > b1) set_bit(selbm, e);
-            else if (d == b1) {
-              const uint32_t pos = atomicAdd(&sh.ncand, 1u);
-              if (pos < (uint32_t)cap) { ckey[pos] = key; cidx[pos] = (uint32_t)e; }
-            }
-          });
+          row, [&](uint32_t key, bool ok) { if (ok && (key >> kShift1) == b1) atomicAdd(&h2[(key >> kShift2) & (kBins2 - 1)], 1u); },
+          [&](uint32_t key) { if ((key >> kShift1) == b1) atomicAdd(&h2[(key >> kShift2) & (kBins2 - 1)], 1u); });
       __syncthreads();
-      select_candidates((int)min(sh.ncand, (uint32_t)cap), b1, rank1);   // == c1 candidates
-    } else {
-      // ---- wide bin: resolve digits 2 and 3 with extra passes over the row
-      for (int j = t; j < kBins2; j += kThreads) hist[j] = 0;
+      const uint32_t rank1 = m - above1;
+      find_bin(h2, kBins2, rank1, L.sh);
+      const uint32_t pre = (b1 << (kShift1 - kShift2)) | L.sh.bin;
+      const uint32_t rank2 = rank1 - L.sh.above;
       __syncthreads();
-      auto h2 = [&](int, uint32_t key) {
-        if ((key >> kShift1) == b1) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
-      };
-      scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h2(e, key); }, h2);
+      zero(h2, kBins3);
       __syncthreads();
-      find_bin(hist, kBins2, rank1, sh);
-      const uint32_t pre = (b1 << (kShift1 - kShift2)) | sh.bin;
-      const uint32_t rank2 = rank1 - sh.above;
+      scan_row(row, [&](uint32_t key, bool ok) { if (ok && (key >> kShift2) == pre) atomicAdd(&h2[key & (kBins3 - 1)], 1u); },
+               [&](uint32_t key) { if ((key >> kShift2) == pre) atomicAdd(&h2[key & (kBins3 - 1)], 1u); });
       __syncthreads();
-      for (int j = t; j < kBins3; j += kThreads) hist[j] = 0;
+      find_bin(h2, kBins3, rank2, L.sh);
+      const uint32_t tau = (pre << kShift2) | L.sh.bin;
+      const uint32_t need = rank2 - L.sh.above;
       __syncthreads();
-      auto h3 = [&](int, uint32_t key) {
-        if ((key >> kShift2) == pre) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
-      };
-      scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) h3(e, key); }, h3);
-      __syncthreads();
-      find_bin(hist, kBins3, rank2, sh);
-      tau = (pre << kShift2) | sh.bin;
-      need = rank2 - sh.above;
-      auto mark = [&](int e, uint32_t key) {
-        if (key > tau) set_bit(selbm, e);
-        else if (key == tau) set_bit(tiebm, e);
-      };
-      scan_row(row, [&](int e, uint32_t key, bool ok) { if (ok) mark(e, key); }, mark);
+      write_selection(row, tau, need, m, out, L.sh);
     }
   }
-  __syncthreads();
-
-  // ---- emit: keep the first `need` ties, then all marked indices ascending
-  const int wpt = (nwords + kThreads - 1) / kThreads;
-  const int w0 = min(t * wpt, nwords), w1 = min(w0 + wpt, nwords);
-  uint32_t tl = 0;
-  for (int w = w0; w < w1; ++w) tl += __popc(tiebm[w]);
-  uint32_t tpre = block_exclusive_scan(tl, sh);
-  uint32_t sl = 0;
-  for (int w = w0; w < w1; ++w) {
-    const uint32_t tw = tiebm[w];
-    const uint32_t c = __popc(tw);
-    uint32_t kept = 0;
-    if (tpre < need) kept = (tpre + c <= need) ? tw : keep_lowest(tw, need - tpre);
-    tpre += c;
-    const uint32_t s = selbm[w] | kept;
-    selbm[w] = s;
-    sl += __popc(s);
+  if (have) {
+    __syncthreads();
+    Slice s;
+    load_slice(ckey, cidx, nc, s);
+    __syncthreads();   // the list may now be overwritten (select_tau reuses hist2 only)
+    uint32_t tau, need;
+    select_tau(s, m, L.hist2, L.sh, tau, need);
+    emit_slices(s, tau, need, m, out, L.sh);
   }
-  uint32_t pos = block_exclusive_scan(sl, sh);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t s = selbm[w];
-    while (s) {
-      const int bit = __ffs(s) - 1;
-      if (pos < (uint32_t)m) out[pos] = (w << 5) + bit;   // exactly m bits are set; guard anyway
-      ++pos;
-      s &= s - 1;
-    }
-  }
-  for (int j = m + t; j < a.k; j += kThreads) out[j] = -1;
+  for (int j = (int)m + t; j < a.k; j += kThreads) out[j] = -1;
 }
 
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int cap) { topk_row<false>(a, cap, Parts{}); }
+__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) { topk_row<false>(a, Parts{}); }
 
-__global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a, int cap, Parts parts) {
-  topk_row<true>(a, cap, parts);
-}
-
-// Candidate capacity of the single-row selection: what the LDS budget
-// leaves, at most kMaxCand (at the largest supported S this is still ~7900,
-// above any plausible cutoff bin).
-int row_cap(const TopkArgs& a, size_t& lds) {
-  const size_t words = (size_t)((a.S + 31) >> 5);
-  const size_t fixed = (kBins1 + 2 * words) * sizeof(uint32_t);
-  const int cap = (int)min((size_t)kMaxCand, (kDynLds - fixed) / (2 * sizeof(uint32_t)));
-  lds = fixed + 2 * (size_t)cap * sizeof(uint32_t);
-  return cap;
-}
-
-hipError_t set_dyn_lds(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
-}
+__global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a, Parts parts) { topk_row<true>(a, parts); }
 
 }  // namespace
 
@@ -546,13 +621,7 @@ int topk_max_kv() { return kMaxKV; }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.rows <= 0 || a.B <= 0) return hipSuccess;
-  size_t lds = 0;
-  const int cap = row_cap(a, lds);
-  static DeviceOnce attr;
-  const hipError_t ae = (hipError_t)device_once(attr, (int)hipErrorInvalidDevice,
-                                                [](int) { return (int)set_dyn_lds((const void*)topk_kernel); });
-  if (ae != hipSuccess) return ae;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a, cap);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -573,26 +642,17 @@ size_t topk_split_bytes(int64_t rows_total, int nparts) {
 hipError_t launch_topk_split(const TopkArgs& a, int nparts, void* ws, hipStream_t st) {
   if (a.rows <= 0 || a.B <= 0) return hipSuccess;
   if (nparts <= 1) return launch_topk(a, st);
+  if (nparts > kBins2 / 2) return hipErrorInvalidValue;
   const size_t n = (size_t)a.B * a.rows * nparts;
   Parts parts;
   parts.cnt = (uint32_t*)ws;
   parts.key = (uint32_t*)((char*)ws + (n * sizeof(uint32_t) + 255) / 256 * 256);
   parts.idx = parts.key + n * kCapPart;
   parts.nparts = nparts;
-  size_t lds = 0;
-  const int cap = row_cap(a, lds);
-  static DeviceOnce attr;
-  const hipError_t ae = (hipError_t)device_once(attr, (int)hipErrorInvalidDevice, [](int) {
-    hipError_t e = set_dyn_lds((const void*)topk_collect_kernel);
-    if (e == hipSuccess) e = set_dyn_lds((const void*)topk_merge_kernel);
-    return (int)e;
-  });
-  if (ae != hipSuccess) return ae;
-  const size_t lds_collect = (kBins1 + 2 * (size_t)kCapPart) * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)n), dim3(kThreads), lds_collect, st, a, parts);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)n), dim3(kThreads), 0, st, a, parts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), lds, st, a, cap, parts);
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)(a.B * a.rows)), dim3(kThreads), 0, st, a, parts);
   return hipGetLastError();
 }
 
