@@ -723,9 +723,14 @@ indexer_decode_kernel(IndexerArgs a) {
   for (int s0 = k_begin; s0 < k_end; s0 += 64) {
     const int s = s0 + lane;   // key whose score this lane ends up holding
     const float ks = ksr.scale(s0, lane);
+    // The next step's keys are loaded ahead.  The last step reloads its own
+    // keys (still in cache) instead: the keys after this wave's range belong
+    // to another wave, usually one long finished on another XCD, so reading
+    // them again went to HBM (one step in eight, 12% of the stream).
+    const int nbase = s0 + 64 < k_end ? s0 + 64 : s0;
     v8i nx[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) nx[u] = ksr.load(s0 + 64 + 16 * u, kl);
+    for (int u = 0; u < 4; ++u) nx[u] = ksr.load(nbase + 16 * u, kl);
     const v8i* kp[4] = {&kt[0], &kt[1], &kt[2], &kt[3]};
     float p[4];
     tile_partials_relu<NHT>(qa, wq, kp, p);

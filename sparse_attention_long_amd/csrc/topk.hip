@@ -173,14 +173,18 @@ __device__ __forceinline__ void scan_row(const RowSplit& r, F&& f, G&& g) {
 
 // The ordered passes: iteration it of a range of float4s starting at q0
 // gives thread t the float4s q0 + (it * kThreads + t) * kVec + u, u < kVec:
-// 16 consecutive scores, so that thread order is element order.  Loads v
-// and the keys of the thread's scores (valid: inside [q0, q1)).
-__device__ __forceinline__ int ordered_keys(const RowSplit& r, int q0, int q1, int it, uint32_t (&keys)[4 * kVec],
-                                            uint32_t& valid) {
+// 16 consecutive scores, so that thread order is element order.
+// ordered_loads issues the loads; keys_of maps them to keys (valid: inside
+// [q0, q1)); ordered_keys does both.
+__device__ __forceinline__ void ordered_loads(const RowSplit& r, int q0, int q1, int it, float4 (&v)[kVec]) {
   const int qb = q0 + (it * kThreads + (int)threadIdx.x) * kVec;
-  float4 v[kVec];
 #pragma unroll
   for (int u = 0; u < kVec; ++u) v[u] = r.xv[qb + u < q1 ? qb + u : q0];
+}
+
+__device__ __forceinline__ int keys_of(const RowSplit& r, int q0, int q1, int it, const float4 (&v)[kVec],
+                                       uint32_t (&keys)[4 * kVec], uint32_t& valid) {
+  const int qb = q0 + (it * kThreads + (int)threadIdx.x) * kVec;
   valid = 0;
 #pragma unroll
   for (int u = 0; u < kVec; ++u) {
@@ -193,11 +197,18 @@ __device__ __forceinline__ int ordered_keys(const RowSplit& r, int q0, int q1, i
   return r.h + 4 * qb;   // element index of keys[0]
 }
 
-// Appends, in ascending element order, every element of the float4 range
-// [q0, q1) whose key is >= lo -- preceded by those of the scalar head
-// elements [0, h) if `head` and followed by those of the tail elements
-// [tail0, n) if `tail` -- to the candidate list (key, idx), counting also
-// past `cap` but storing only below it.  Returns the count (block-uniform).
+__device__ __forceinline__ int ordered_keys(const RowSplit& r, int q0, int q1, int it, uint32_t (&keys)[4 * kVec],
+                                            uint32_t& valid) {
+  float4 v[kVec];
+  ordered_loads(r, q0, q1, it, v);
+  return keys_of(r, q0, q1, it, v, keys, valid);
+}
+
+// Collects the keys >= lo of float4s [q0, q1) (and, for head / tail, of the
+// row's scalar head and tail) into ckey / cidx in element order; returns
+// their count (entries past cap are counted, not stored).  Each iteration's
+// loads are issued before the previous iteration's block scan, so the scan's
+// barriers overlap the memory latency.
 __device__ uint32_t collect_ordered(const RowSplit& r, int q0, int q1, bool head, bool tail, uint32_t lo,
                                     uint32_t* ckey, uint32_t* cidx, uint32_t cap, Shared& sh) {
   const int t = threadIdx.x;
@@ -219,9 +230,15 @@ __device__ uint32_t collect_ordered(const RowSplit& r, int q0, int q1, bool head
     __syncthreads();
   }
   const int iters = (q1 - q0 + kThreads * kVec - 1) / (kThreads * kVec);
+  float4 nv[kVec];
+  if (iters > 0) ordered_loads(r, q0, q1, 0, nv);
   for (int it = 0; it < iters; ++it) {
+    float4 v[kVec];
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) v[u] = nv[u];
+    if (it + 1 < iters) ordered_loads(r, q0, q1, it + 1, nv);
     uint32_t keys[4 * kVec], valid;
-    const int e0 = ordered_keys(r, q0, q1, it, keys, valid);
+    const int e0 = keys_of(r, q0, q1, it, v, keys, valid);
     uint32_t cm = 0;
 #pragma unroll
     for (int j = 0; j < 4 * kVec; ++j) cm |= (keys[j] >= lo ? 1u : 0u) << j;
@@ -309,28 +326,56 @@ __device__ void select_tau(const Slice& s, uint32_t m, uint32_t* hist, Shared& s
   int hi = kmax == kmin ? -1 : 31 - __clz(kmax ^ kmin);   // highest differing bit
   uint32_t pmask = hi < 0 ? 0xFFFFFFFFu : hi >= 31 ? 0u : ~((2u << hi) - 1u);
   uint32_t prefix = kmax & pmask, rank = m;
+  // Two 256-bin histograms alternate between rounds: a round fills one and
+  // clears the other, and wave 0 alone finds the bin, so a round needs two
+  // barriers.
+  uint32_t* hc = hist;
+  uint32_t* hn = hist + 256;
+  if (t < 256) hc[t] = 0u;
+  __syncthreads();
   while (hi >= 0) {   // block-uniform
     const int lo_bit = max(hi - 7, 0);
     const uint32_t dmask = (2u << (hi - lo_bit)) - 1u;
-    if (t < 256) hist[t] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kSlice; ++u)
-      if ((uint32_t)u < s.n && (s.key[u] & pmask) == prefix) atomicAdd(&hist[(s.key[u] >> lo_bit) & dmask], 1u);
+      if ((uint32_t)u < s.n && (s.key[u] & pmask) == prefix) atomicAdd(&hc[(s.key[u] >> lo_bit) & dmask], 1u);
+    if (t < 256) hn[t] = 0u;
     __syncthreads();
-    const uint32_t c = t < 256 ? hist[255 - t] : 0u;   // thread t < 256 owns bin 255 - t
-    uint32_t tot;
-    const uint32_t above = block_scan(c, tot, sh);
-    if (c > 0 && above < rank && rank <= above + c) {
-      sh.bin = (uint32_t)(255 - t);
-      sh.above = above;
+    if (t < kWave) {
+      // lane l owns bins 255 - 4l - j (j < 4): lane order is bin order from the top
+      uint32_t c[4], local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hc[255 - 4 * t - j];
+        local += c[j];
+      }
+      uint32_t incl = local;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_up(incl, d, kWave);
+        if (t >= d) incl += y;
+      }
+      uint32_t cum = incl - local;
+      if (local > 0 && cum < rank && rank <= incl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= rank) {
+            sh.bin = (uint32_t)(255 - 4 * t - j);
+            sh.above = cum;
+            break;
+          }
+          cum += c[j];
+        }
+      }
     }
     __syncthreads();
     prefix |= sh.bin << lo_bit;
     pmask |= dmask << lo_bit;
     rank -= sh.above;
     hi = lo_bit - 1;
-    __syncthreads();
+    uint32_t* tmp = hc;
+    hc = hn;
+    hn = tmp;
   }
   tau = prefix;
   need = rank;
@@ -424,10 +469,15 @@ __device__ void write_selection(const RowSplit& r, uint32_t tau, uint32_t need, 
   __syncthreads();
 }
 
+__device__ __forceinline__ void zero(uint32_t* p, int n) {
+  for (int j = threadIdx.x; j < n; j += kThreads) p[j] = 0u;
+}
+
 // Sampled cutoff of a row: 32 blocks of 64 scores spread over the row give
 // a conservative lower bound lo for tau (the sample's rank-r 13-bit bin, r
 // chosen so that about 2m keys are expected at or above it).  hist (kBins1)
-// must be zero on entry.  A row of fewer than 64 scores has no room for the
+// is cleared here, after the sample loads are issued, so that their latency
+// overlaps the clearing.  A row of fewer than 64 scores has no room for the
 // sample blocks: its cutoff is 0, the lowest key, so every score becomes a
 // candidate (n < 64 fits any candidate list).  n is block-uniform, so the
 // early return keeps the barriers uniform.
@@ -440,16 +490,17 @@ __device__ __forceinline__ uint32_t sampled_cutoff(const RowSplit& row, int n, i
   const int t = threadIdx.x;
   const int blk = t / kTpb;
   const int e0 = (int)(((int64_t)blk * (n - 64)) / 31) + kPer * (t % kTpb);
+  float x[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) atomicAdd(&hist[order_key(row.x[e0 + j]) >> kShift1], 1u);
+  for (int j = 0; j < kPer; ++j) x[j] = row.x[e0 + j];
+  zero(hist, kBins1);   // while the sample loads are in flight
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) atomicAdd(&hist[order_key(x[j]) >> kShift1], 1u);
   __syncthreads();
   const uint32_t r = (uint32_t)min(2048ll, ((int64_t)2 * m * 2048 + n - 1) / n);
   find_bin(hist, kBins1, r, sh);
   return sh.bin << kShift1;
-}
-
-__device__ __forceinline__ void zero(uint32_t* p, int n) {
-  for (int j = threadIdx.x; j < n; j += kThreads) p[j] = 0u;
 }
 
 // Candidates of a row collected by the parts of topk_collect_kernel, each
@@ -480,8 +531,6 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(TopkArgs a, Part
     return;
   }
   const RowSplit row(a.scores + ((int64_t)b * a.sc_rows_b + i) * a.ld, n);
-  zero(L.u.hist1, kBins1);
-  __syncthreads();
   const uint32_t lo = sampled_cutoff(row, n, m, L.u.hist1, L.sh);
   const int q0 = (int)((int64_t)row.nq * f / parts.nparts), q1 = (int)((int64_t)row.nq * (f + 1) / parts.nparts);
   const uint32_t nc = collect_ordered(row, q0, q1, f == 0, f == parts.nparts - 1, lo, L.u.c.key, L.u.c.idx,
@@ -549,8 +598,6 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, const Parts& parts) 
     __syncthreads();
   }
   if (!have) {
-    zero(L.u.hist1, kBins1);
-    __syncthreads();
     const uint32_t lo = sampled_cutoff(row, n, (int)m, L.u.hist1, L.sh);
     nc = collect_ordered(row, 0, row.nq, true, true, lo, ckey, cidx, kCap, L.sh);
     have = nc >= m && nc <= (uint32_t)kCap;
