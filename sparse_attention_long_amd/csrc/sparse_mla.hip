@@ -183,9 +183,45 @@ struct RowGather {
       dma_x4_s((uint32_t)off_b, kvb, t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u);
     }
   }
+  // All of a wave's copies for one chunk.  Dense caches: the lane offsets
+  // and LDS targets are formed first and the nine copies then go out from
+  // one asm block that sets M0 before each, so the copies do not wait on
+  // one another's address arithmetic (the same copies in the same order as
+  // issue(0..kPerWave-1)).
   __device__ __forceinline__ void issue_all(uint16_t* tile, const uint16_t* kvb, int wave) const {
+    if constexpr (!K64) {
+      static_assert(kPerWave == 9, "eight part-A rows and one part-B block per wave");
+      const uint32_t t0 = lds_addr(tile);
+      uint32_t vo[8], la[8];
 #pragma unroll
-    for (int jj = 0; jj < kPerWave; ++jj) issue(jj, tile, kvb, wave);
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = jj * NW + wave;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)off_a, j);
+        vo[jj] = (lane16 ^ (16u * (uint32_t)(jj & 3))) + lo;
+        la[jj] = t0 + (uint32_t)j * (C::kRA * 16);
+      }
+      const uint32_t lb = t0 + (uint32_t)(C::kBaseB + wave * kWave) * 16u;
+      uint32_t saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %11\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %10\n\t"
+          "s_mov_b32 m0, %12\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %10\n\t"
+          "s_mov_b32 m0, %13\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %10\n\t"
+          "s_mov_b32 m0, %14\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %10\n\t"
+          "s_mov_b32 m0, %15\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %10\n\t"
+          "s_mov_b32 m0, %16\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %10\n\t"
+          "s_mov_b32 m0, %17\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
+          "s_mov_b32 m0, %18\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+          "s_mov_b32 m0, %19\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %10\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "v"(vo[5]), "v"(vo[6]), "v"(vo[7]),
+            "v"((uint32_t)off_b), "s"(kvb), "s"(la[0]), "s"(la[1]), "s"(la[2]), "s"(la[3]), "s"(la[4]),
+            "s"(la[5]), "s"(la[6]), "s"(la[7]), "s"(lb));
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < kPerWave; ++jj) issue(jj, tile, kvb, wave);
+    }
   }
 };
 
