@@ -78,6 +78,7 @@ struct RowLds {
 };
 static_assert(2 * kCap >= kBins1 && 2 * kCapPart >= kBins1, "the histogram fits the candidate space");
 static_assert(2048 % kThreads == 0 && kThreads >= 256 && kCap % kThreads == 0, "sample and slice shapes");
+static_assert(kCap < 65536, "emission packs two candidate counts in one word");
 
 // Exclusive prefix sum over the block in thread order, and the block total.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, Shared& sh) {
@@ -383,29 +384,32 @@ __device__ void select_tau(const Slice& s, uint32_t m, uint32_t* hist, Shared& s
 
 // Writes the selection from the slices (which are in element order): every
 // key above tau and the first `need` keys equal to tau, in element order.
+// One block scan gives each thread both the keys above tau and the keys
+// equal to tau held by the threads before it (each count is below 2^16,
+// packed in one word); a kept key's slot is then (keys above tau before it)
+// + min(keys equal to tau before it, need).
 __device__ void emit_slices(const Slice& s, uint32_t tau, uint32_t need, uint32_t m, int32_t* out, Shared& sh) {
-  uint32_t ties = 0;
+  uint32_t above = 0, ties = 0;
 #pragma unroll
-  for (int u = 0; u < kSlice; ++u) ties += (uint32_t)u < s.n && s.key[u] == tau ? 1u : 0u;
-  uint32_t tot;
-  const uint32_t tie0 = block_scan(ties, tot, sh);
-  uint32_t keep = 0;
-  {
-    uint32_t tr = tie0;
-#pragma unroll
-    for (int u = 0; u < kSlice; ++u) {
-      if ((uint32_t)u >= s.n) continue;
-      if (s.key[u] > tau) ++keep;
-      else if (s.key[u] == tau) keep += tr++ < need ? 1u : 0u;
-    }
+  for (int u = 0; u < kSlice; ++u) {
+    const bool in = (uint32_t)u < s.n;
+    above += in && s.key[u] > tau ? 1u : 0u;
+    ties += in && s.key[u] == tau ? 1u : 0u;
   }
-  uint32_t pos = block_scan(keep, tot, sh);
-  uint32_t tr = tie0;
+  uint32_t tot;
+  const uint32_t before = block_scan(above | (ties << 16), tot, sh);
+  uint32_t a = before & 0xFFFFu, t = before >> 16;
 #pragma unroll
   for (int u = 0; u < kSlice; ++u) {
     if ((uint32_t)u >= s.n) continue;
-    const bool k = s.key[u] > tau || (s.key[u] == tau && tr++ < need);
-    if (k && pos < m) out[pos++] = (int32_t)s.idx[u];
+    if (s.key[u] > tau) {
+      const uint32_t pos = a + min(t, need);
+      if (pos < m) out[pos] = (int32_t)s.idx[u];
+      ++a;
+    } else if (s.key[u] == tau) {
+      if (t < need && a + t < m) out[a + t] = (int32_t)s.idx[u];
+      ++t;
+    }
   }
 }
 
