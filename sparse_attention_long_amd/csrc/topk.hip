@@ -58,7 +58,7 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 struct Shared {
-  uint32_t scan[kWaves];
+  uint32_t scan[2][kWaves];   // block_scan's wave totals, two buffers
   uint32_t bin, above, total, flag;
 };
 
@@ -81,7 +81,11 @@ static_assert(2048 % kThreads == 0 && kThreads >= 256 && kCap % kThreads == 0, "
 static_assert(kCap < 65536, "emission packs two candidate counts in one word");
 
 // Exclusive prefix sum over the block in thread order, and the block total.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, Shared& sh) {
+// One barrier: the wave totals go to buffer `buf`, and a scan that follows
+// another with no barrier in between must use the other buffer (a wave can
+// then only overwrite a buffer after every wave has passed the barrier of
+// the scan in between, i.e. has finished reading it).
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, Shared& sh, int buf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -89,16 +93,15 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, Shar
     const uint32_t y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
-  if (lane == 63) sh.scan[wave] = x;
+  if (lane == 63) sh.scan[buf][wave] = x;
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const uint32_t s = sh.scan[w];
+    const uint32_t s = sh.scan[buf][w];
     pre += w < wave ? s : 0u;
     tot += s;
   }
-  __syncthreads();
   total = tot;
   return pre + x - v;
 }
@@ -114,7 +117,7 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t rank, Shared&
   for (int j = 0; j < per; ++j)
     if (top - j >= 0) local += hist[top - j];
   uint32_t tot;
-  const uint32_t excl = block_scan(local, tot, sh);
+  const uint32_t excl = block_scan(local, tot, sh, 0);   // a barrier follows
   if (local > 0 && excl < rank && rank <= excl + local) {
     uint32_t cum = excl;
     for (int j = 0; j < per && top - j >= 0; ++j) {
@@ -245,7 +248,7 @@ __device__ uint32_t collect_ordered(const RowSplit& r, int q0, int q1, bool head
     for (int j = 0; j < 4 * kVec; ++j) cm |= (keys[j] >= lo ? 1u : 0u) << j;
     cm &= valid;
     uint32_t tot;
-    uint32_t pos = base + block_scan((uint32_t)__popc(cm), tot, sh);
+    uint32_t pos = base + block_scan((uint32_t)__popc(cm), tot, sh, it & 1);
 #pragma unroll
     for (int j = 0; j < 4 * kVec; ++j)
       if ((cm >> j) & 1u) {
@@ -397,7 +400,7 @@ __device__ void emit_slices(const Slice& s, uint32_t tau, uint32_t need, uint32_
     ties += in && s.key[u] == tau ? 1u : 0u;
   }
   uint32_t tot;
-  const uint32_t before = block_scan(above | (ties << 16), tot, sh);
+  const uint32_t before = block_scan(above | (ties << 16), tot, sh, 0);
   uint32_t a = before & 0xFFFFu, t = before >> 16;
 #pragma unroll
   for (int u = 0; u < kSlice; ++u) {
@@ -452,14 +455,14 @@ __device__ void write_selection(const RowSplit& r, uint32_t tau, uint32_t need, 
     gt &= valid;
     eq &= valid;
     uint32_t ttot;
-    const uint32_t tpre = tbase + block_scan((uint32_t)__popc(eq), ttot, sh);
+    const uint32_t tpre = tbase + block_scan((uint32_t)__popc(eq), ttot, sh, 0);
     // this thread's kept ties: those whose rank tpre + (ties before) < need
     uint32_t keepm = gt, tr = tpre;
 #pragma unroll
     for (int j = 0; j < 4 * kVec; ++j)
       if ((eq >> j) & 1u) keepm |= (tr++ < need ? 1u : 0u) << j;
     uint32_t ktot;
-    uint32_t pos = base + block_scan((uint32_t)__popc(keepm), ktot, sh);
+    uint32_t pos = base + block_scan((uint32_t)__popc(keepm), ktot, sh, 1);
 #pragma unroll
     for (int j = 0; j < 4 * kVec; ++j)
       if ((keepm >> j) & 1u) {
