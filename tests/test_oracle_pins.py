@@ -510,6 +510,35 @@ def test_masked_mha_single_key_and_empty_rows():
     assert np.array_equal(o, np.zeros_like(o)) and np.all(lse == -np.inf)
 
 
+def test_mha_decompress_worked_example():
+    # MHA mode (the analysis page, Fig. 7 discussion): per-head keys
+    # k_nope[h, s] = W_UK[h] c_s and values v[h, s] = W_UV[h] c_s over the
+    # first dim_v latent dims; the remaining dims are the shared rope part.
+    # Worked by hand on two latent rows, dim_v = 3, rope 2, two heads;
+    # rectangular W (2 x 3 and 1 x 3) so a transposed matrix cannot pass.
+    kv = np.array([[1.0, 2.0, 3.0, 10.0, 20.0],
+                   [4.0, 5.0, 6.0, 30.0, 40.0]])
+    w_uk = np.array([[[1.0, 0.0, 0.0], [0.0, 0.0, 2.0]],
+                     [[0.0, 1.0, 0.0], [1.0, 1.0, 1.0]]])
+    w_uv = np.array([[[0.0, 1.0, 0.0]],
+                     [[1.0, 0.0, -1.0]]])
+    k_nope, v, rope = O.mha_decompress(kv, w_uk, w_uv, 3)
+    assert k_nope.shape == (2, 2, 2) and v.shape == (2, 2, 1) and rope.shape == (2, 2)
+    assert np.array_equal(k_nope[0], [[1.0, 6.0], [4.0, 12.0]])     # [c0, 2 c2]
+    assert np.array_equal(k_nope[1], [[2.0, 6.0], [5.0, 15.0]])     # [c1, c0 + c1 + c2]
+    assert np.array_equal(v[0], [[2.0], [5.0]])                     # c1
+    assert np.array_equal(v[1], [[-2.0], [-2.0]])                   # c0 - c2
+    assert np.array_equal(rope, [[10.0, 20.0], [30.0, 40.0]])
+
+
+def test_candidate_and_selection_counts():
+    # n_p = min(p + 1, S) causal candidates; m_p = min(k, n_p) selected
+    # (Sec. 5.1 of the analysis page: a short row keeps everything it has).
+    assert [O.n_candidates(p, 10) for p in (0, 4, 9, 12)] == [1, 5, 10, 10]
+    assert [O.n_selected(p, 10, 4) for p in (0, 2, 3, 9)] == [1, 3, 4, 4]
+    assert O.n_selected(9, 10, 16) == 10
+
+
 def test_selection_mask_bits():
     m = O.selection_mask(np.array([0, 3, 3, 31, 32, -1, 40, 7]), 33)
     assert np.flatnonzero(m).tolist() == [0, 3, 7, 31, 32]
