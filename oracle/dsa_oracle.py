@@ -82,7 +82,7 @@ def dequant_e4m3(codes, scales) -> np.ndarray:
 # ----------------------------------------------------------------- quantisation
 def quantize_e4m3_tokens(x):
     """Per-token FP8 quantisation (the FP8 indexer inputs of Sec. 1.1, in the
-    format and scale granularity this build reads into the pages): scale =
+    format and scale granularity read into the pages here): scale =
     amax / 448 in float32 (1 for an all-zero token); each value is divided by
     the scale in float32 and rounded to the nearest E4M3FN value, ties to the
     even code, with magnitudes of 448 and above saturating to 448.  The sign
