@@ -80,6 +80,10 @@ static_assert(2 * kCap >= kBins1 && 2 * kCapPart >= kBins1, "the histogram fits 
 static_assert(2048 % kThreads == 0 && kThreads >= 256 && kCap % kThreads == 0, "sample and slice shapes");
 static_assert(kCap < 65536, "emission packs two candidate counts in one word");
 
+__device__ __forceinline__ void zero(uint32_t* p, int n) {
+  for (int j = threadIdx.x; j < n; j += kThreads) p[j] = 0u;
+}
+
 // Exclusive prefix sum over the block in thread order, and the block total.
 // One barrier: the wave totals go to buffer `buf`, and a scan that follows
 // another with no barrier in between must use the other buffer (a wave can
@@ -300,7 +304,8 @@ __device__ __forceinline__ void load_slice(const uint32_t* ckey, const uint32_t*
 // The bits every candidate shares (above the highest bit where the largest
 // and smallest keys differ) are fixed at once; the rest are resolved 8 at
 // a time from the top, with a 256-bin histogram in `hist`.
-__device__ void select_tau(const Slice& s, uint32_t m, uint32_t* hist, Shared& sh, uint32_t& tau, uint32_t& need) {
+__device__ void select_tau(const Slice& s, uint32_t m, uint32_t* hist, uint32_t* wide, Shared& sh, uint32_t& tau,
+                           uint32_t& need) {
   const int t = threadIdx.x;
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
@@ -330,9 +335,31 @@ __device__ void select_tau(const Slice& s, uint32_t m, uint32_t* hist, Shared& s
   int hi = kmax == kmin ? -1 : 31 - __clz(kmax ^ kmin);   // highest differing bit
   uint32_t pmask = hi < 0 ? 0xFFFFFFFFu : hi >= 31 ? 0u : ~((2u << hi) - 1u);
   uint32_t prefix = kmax & pmask, rank = m;
-  // Two 256-bin histograms alternate between rounds: a round fills one and
-  // clears the other, and wave 0 alone finds the bin, so a round needs two
-  // barriers.
+  // First round, when more than 8 bits vary: an 11-bit digit over up to 2048
+  // bins in `wide` (the candidate list's space, free once the slices are
+  // loaded).  The top digit below the common prefix is the crowded one
+  // (most candidates lie just above the cutoff); 8 times as many bins keep
+  // their LDS atomics from piling onto a few addresses, and the round
+  // covers 3 more bits.
+  if (hi >= 8) {
+    const int lo_bit = hi - 10 > 0 ? hi - 10 : 0;
+    const int nbins = 2 << (hi - lo_bit);
+    const uint32_t dmask = (uint32_t)nbins - 1u;
+    zero(wide, nbins);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSlice; ++u)
+      if ((uint32_t)u < s.n) atomicAdd(&wide[(s.key[u] >> lo_bit) & dmask], 1u);
+    __syncthreads();
+    find_bin(wide, nbins, rank, sh);   // ends with a barrier
+    prefix |= sh.bin << lo_bit;
+    pmask |= dmask << lo_bit;
+    rank -= sh.above;
+    hi = lo_bit - 1;
+  }
+  // Two 256-bin histograms alternate between the remaining rounds: a round
+  // fills one and clears the other, and wave 0 alone finds the bin, so a
+  // round needs two barriers.
   uint32_t* hc = hist;
   uint32_t* hn = hist + 256;
   if (t < 256) hc[t] = 0u;
@@ -474,10 +501,6 @@ __device__ void write_selection(const RowSplit& r, uint32_t tau, uint32_t need, 
   }
   if (r.tail0 < r.n && t == 0) serial(r.tail0, r.n);
   __syncthreads();
-}
-
-__device__ __forceinline__ void zero(uint32_t* p, int n) {
-  for (int j = threadIdx.x; j < n; j += kThreads) p[j] = 0u;
 }
 
 // Sampled cutoff of a row: 32 blocks of 64 scores spread over the row give
@@ -657,9 +680,9 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, const Parts& parts) 
     __syncthreads();
     Slice s;
     load_slice(ckey, cidx, nc, s);
-    __syncthreads();   // the list may now be overwritten (select_tau reuses hist2 only)
+    __syncthreads();   // the list may now be overwritten: select_tau takes its space
     uint32_t tau, need;
-    select_tau(s, m, L.hist2, L.sh, tau, need);
+    select_tau(s, m, L.hist2, L.u.hist1, L.sh, tau, need);
     emit_slices(s, tau, need, m, out, L.sh);
   }
   for (int j = (int)m + t; j < a.k; j += kThreads) out[j] = -1;
