@@ -694,7 +694,12 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, TileMap map) {
 }
 
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeKeysPerWave = 512;
+// Keys per wave of the decode form.  With 3 waves per SIMD (156 VGPRs) the
+// GPU holds 3072 waves at once, and a 64-sequence 128K step has 32768 waves
+// of 256 keys (10.7 rounds); shorter ranges leave a smaller tail in the last
+// round.  Per 64 x 128K decode step: 343, 339, 326 and 323 us for 2048,
+// 1024, 512 and 256 keys per wave.
+constexpr int kDecodeKeysPerWave = 256;
 
 template <int NHT, bool kFullD>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
