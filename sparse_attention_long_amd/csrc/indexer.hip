@@ -631,17 +631,20 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, TileMap map) {
 
   // One step: the MFMAs and epilogue of step st with operands (kt0, kt1,
   // ks) while the operands of step st+1 are read from (nk, ns) at
-  // sub-block step nsst into (nt0, nt1, nks).
+  // sub-block step nsst into (nt0, nt1, nks).  The score and its store
+  // offset are returned; put() stores them.
   auto body = [&](int st, const v8i& kt0, const v8i& kt1, float ks, const uint8_t* nk, const float* ns, int nsst,
-                  v8i& nt0, v8i& nt1, float& nks) {
+                  v8i& nt0, v8i& nt1, float& nks, float& val, int& off) {
     read_step(nk, ns, nsst, nt0, nt1, nks);
     const v8i* kp[4] = {&kt0, &kt1, &kt0, &kt1};
     float p[4];
     tile_partials<NHT>(qp, wp, kp, lin, p);
-    const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
+    val = reduce_scatter4(p[0], p[1], p[2], p[3]) * ks;
     const int s = k_begin + 32 * st + 16 * (g & 1) + kl16;
-    const int off = s < my_np ? lane_row_off + s * 4 : INT_MAX;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, off, 0, 0);
+    off = s < my_np ? lane_row_off + s * 4 : INT_MAX;
+  };
+  auto put = [&](float val, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), out_rsrc, off, 0, 0);
   };
   // The 8 steps of sub-block j from buffer (ck, cs); the last one reads the
   // first operands of sub-block j+1 from (ok, os) after the barrier that
@@ -651,20 +654,32 @@ indexer_prefill_lds_kernel(IndexerArgs a, int keys_per_wg, TileMap map) {
   float ksA, ksB;
   auto sub_block = [&](int j, uint8_t* ck, float* cs, uint8_t* ok, float* os) {
     const int st0 = 8 * j;
+    float val;
+    int off;
 #pragma unroll
     for (int sst = 0; sst < 8; sst += 2) {
       if (st0 + sst >= nsteps) return;
       if (sst == 6) {
-        body(st0 + 6, ktA0, ktA1, ksA, ck, cs, 7, ktB0, ktB1, ksB);
-        if (st0 + 7 >= nsteps) return;
+        body(st0 + 6, ktA0, ktA1, ksA, ck, cs, 7, ktB0, ktB1, ksB, val, off);
+        if (st0 + 7 >= nsteps) {
+          put(val, off);
+          return;
+        }
+        // The DMA wait also waits for this wave's score stores (they count
+        // in the same counter), so step 6's store goes out after it: the
+        // wait then covers only stores a step or more old, not a fresh one.
         wait_dma();
+        put(val, off);
         __syncthreads();   // sub-block j+1 staged; everyone is done reading buffer (ck, cs)
         if (j + 2 < nsub) dma(j + 2, ck, cs);
-        body(st0 + 7, ktB0, ktB1, ksB, ok, os, 0, ktA0, ktA1, ksA);
+        body(st0 + 7, ktB0, ktB1, ksB, ok, os, 0, ktA0, ktA1, ksA, val, off);
+        put(val, off);
       } else {
-        body(st0 + sst, ktA0, ktA1, ksA, ck, cs, sst + 1, ktB0, ktB1, ksB);
+        body(st0 + sst, ktA0, ktA1, ksA, ck, cs, sst + 1, ktB0, ktB1, ksB, val, off);
+        put(val, off);
         if (st0 + sst + 1 >= nsteps) return;
-        body(st0 + sst + 1, ktB0, ktB1, ksB, ck, cs, sst + 2, ktA0, ktA1, ksA);
+        body(st0 + sst + 1, ktB0, ktB1, ksB, ck, cs, sst + 2, ktA0, ktA1, ksA, val, off);
+        put(val, off);
       }
     }
   };

@@ -596,6 +596,8 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, const Parts& parts) 
   uint32_t* cidx = L.u.c.idx;
   uint32_t nc = 0;
   bool have = false;   // block-uniform: [0, nc) of the list holds every key >= some cutoff, m <= nc <= kCap
+  bool sliced = false;   // block-uniform: the slices already hold the list (loaded from the parts)
+  Slice s;
   if constexpr (kParts) {
     // the parts' counts, one load per thread
     if (t < parts.nparts) L.hist2[t] = parts.cnt[(int64_t)blockIdx.x * parts.nparts + t];
@@ -614,16 +616,34 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, const Parts& parts) 
     }
     __syncthreads();
     if (L.sh.flag) {
+      // The list is the parts' lists back to back.  Each thread loads its
+      // slice of it (the positions load_slice gives it) straight from the
+      // parts, all loads in flight at once; part f's list starts at list
+      // position off[f] and at workspace element (row * nparts + f) * kCapPart.
       nc = L.sh.total;
-      for (int f = 0; f < parts.nparts; ++f) {
-        const uint32_t c = L.hist2[f], off = L.hist2[kBins2 / 2 + f];
-        const int64_t base = ((int64_t)blockIdx.x * parts.nparts + f) * kCapPart;
-        for (int j = t; j < (int)c; j += kThreads) {
-          ckey[off + j] = parts.key[base + j];
-          cidx[off + j] = parts.idx[base + j];
+      const uint32_t* off = L.hist2 + kBins2 / 2;
+      const int np = parts.nparts;
+      const uint32_t per = (nc + kThreads - 1) / kThreads;
+      const uint32_t j0 = min((uint32_t)t * per, nc);
+      s.n = min(j0 + per, nc) - j0;
+      const int64_t rowbase = (int64_t)blockIdx.x * np * kCapPart;
+      int f = 0;
+      uint32_t lo_f = 0u, hi_f = np > 1 ? off[1] : 0xFFFFFFFFu;   // part f spans list positions [lo_f, hi_f)
+#pragma unroll
+      for (int u = 0; u < kSlice; ++u) {
+        const uint32_t j = j0 + u;
+        const bool ok = (uint32_t)u < s.n;
+        while (ok && j >= hi_f) {   // empty parts are skipped too
+          ++f;
+          lo_f = hi_f;
+          hi_f = f + 1 < np ? off[f + 1] : 0xFFFFFFFFu;
         }
+        const int64_t src = rowbase + (int64_t)f * kCapPart + (j - lo_f);
+        s.key[u] = ok ? parts.key[src] : 0u;
+        s.idx[u] = ok ? parts.idx[src] : 0u;
       }
       have = true;
+      sliced = true;
     }
     __syncthreads();
   }
@@ -677,10 +697,11 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, const Parts& parts) 
     }
   }
   if (have) {
-    __syncthreads();
-    Slice s;
-    load_slice(ckey, cidx, nc, s);
-    __syncthreads();   // the list may now be overwritten: select_tau takes its space
+    if (!sliced) {
+      __syncthreads();
+      load_slice(ckey, cidx, nc, s);
+    }
+    __syncthreads();   // the list (or the part offsets) may now be overwritten: select_tau takes their space
     uint32_t tau, need;
     select_tau(s, m, L.hist2, L.u.hist1, L.sh, tau, need);
     emit_slices(s, tau, need, m, out, L.sh);
