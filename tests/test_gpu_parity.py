@@ -182,6 +182,39 @@ def test_topk_ws_equals_topk():
         assert np.array_equal(c[B - 1, T - 1].cpu().numpy(), want)
 
 
+def test_topk_ws_candidates_in_few_parts():
+    # Rows whose candidates all sit in one or two of the split collection's
+    # parts: the merge assembles each thread's slice of the candidate list
+    # from the parts, skipping the empty ones.  Increasing scores put every
+    # candidate in the last part, decreasing in the first, a V shape in the
+    # two end parts with empty parts between, a bump in the middle parts.
+    # The sampled cutoff keeps about 2k candidates: with k = 512 they fit one
+    # part's list (8 parts per row here); with k = 2048 a single part's list
+    # can overflow, and the merge falls back to its own pass over the row.
+    rs = np.random.RandomState(14)
+    for B, S, k in ((8, 65536, 512), (64, 131072, 2048)):
+        T = 1
+        j = np.arange(S, dtype=np.float64)
+        shapes = [j, S - j, np.abs(j - S / 2), -np.abs(j - S / 2)]
+        x = np.stack([shapes[b % 4] + 0.25 * rs.rand(S) for b in range(B)]).astype(np.float32)[:, None, :]
+        dims = dsa.Dims(batch=B, n_q=T, n_kv=S, q_pos0=S - T, idx_heads=64, idx_dim=128, heads=128, dim_qk=576,
+                        dim_v=512, topk=k)
+        nws = dsa.dsa.dsa_topk_workspace_size(dims)
+        assert nws > 0
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        xs = to_dev(x)
+        a = torch.full((B, T, k), -7, dtype=torch.int32, device="cuda")
+        c = torch.full((B, T, k), -7, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk(dims, xs, S, a)
+        dsa.dsa.dsa_topk_ws(dims, xs, S, c, ws, nws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, c), (B, S)
+        got = c.cpu().numpy()
+        for b in range(4):
+            assert np.array_equal(got[b, 0], O.topk_row(x[b, 0], k)), (B, S, b)
+        _say("split top-k, candidates in few parts", B, "rows of", S, "keys: equal to dsa_topk and the oracle")
+
+
 def test_validate_counts_planted_values():
     """dsa_validate counts exactly the bad values planted on the host."""
     D = dsa.dsa
