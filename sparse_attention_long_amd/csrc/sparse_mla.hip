@@ -43,6 +43,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRefHeadroom = 64.0f;  // log2 units a logit may exceed the reference by
 constexpr int kMaxSlots = 2048;
+constexpr int kMaxSplits = 16;        // slot splits per row (the split rule caps them)
 constexpr int kLookA = 3;              // QK operand prefetch depth (K steps)
 constexpr int kLookV = 4;              // PV operand prefetch depth (MFMAs)
 
@@ -900,24 +901,41 @@ __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
   const int b = rowid / a.rows, i = rowid % a.rows;
   const int64_t qrow = (int64_t)b * a.qrows_b + i;
   const float* pl = a.part_lse + (int64_t)rowid * a.nsplit * a.H + h;
-  float mx = -INFINITY;
-  for (int j = 0; j < a.nsplit; ++j) mx = fmaxf(mx, pl[(int64_t)j * a.H]);
-  float den = 0.f;
-  if (mx > -INFINITY)
-    for (int j = 0; j < a.nsplit; ++j) den += __expf(pl[(int64_t)j * a.H] - mx);
-  const float lse = mx > -INFINITY ? mx + __logf(den) : -INFINITY;
   const int d = threadIdx.x * 4;
+  const uint16_t* po = a.part_o + ((int64_t)rowid * a.nsplit * a.H + h) * DV + d;
+  const int64_t pstride = (int64_t)a.H * DV;
+  // Every split's log-sum-exp and partial are loaded before the first is
+  // used, so a thread waits for one memory round trip, not one per split
+  // (an empty split's partial is zeros, written by the split kernel).
+  float lv[kMaxSplits];
+  uint2 pv[kMaxSplits];
+#pragma unroll
+  for (int j = 0; j < kMaxSplits; ++j)
+    if (j < a.nsplit) {
+      lv[j] = pl[(int64_t)j * a.H];
+      pv[j] = *(const uint2*)(po + j * pstride);
+    }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxSplits; ++j)
+    if (j < a.nsplit) mx = fmaxf(mx, lv[j]);
+  float den = 0.f;
+  if (mx > -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kMaxSplits; ++j)
+      if (j < a.nsplit) den += __expf(lv[j] - mx);
+  }
+  const float lse = mx > -INFINITY ? mx + __logf(den) : -INFINITY;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   if (mx > -INFINITY) {
-    for (int j = 0; j < a.nsplit; ++j) {
-      const float lj = pl[(int64_t)j * a.H];
-      if (lj == -INFINITY) continue;
-      const float wj = __expf(lj - lse);
-      const uint2 pk = *(const uint2*)(a.part_o + (((int64_t)rowid * a.nsplit + j) * a.H + h) * DV + d);
-      acc.x += wj * __uint_as_float(pk.x << 16);
-      acc.y += wj * __uint_as_float(pk.x & 0xFFFF0000u);
-      acc.z += wj * __uint_as_float(pk.y << 16);
-      acc.w += wj * __uint_as_float(pk.y & 0xFFFF0000u);
+#pragma unroll
+    for (int j = 0; j < kMaxSplits; ++j) {
+      if (j >= a.nsplit || lv[j] == -INFINITY) continue;
+      const float wj = __expf(lv[j] - lse);
+      acc.x += wj * __uint_as_float(pv[j].x << 16);
+      acc.y += wj * __uint_as_float(pv[j].x & 0xFFFF0000u);
+      acc.z += wj * __uint_as_float(pv[j].y << 16);
+      acc.w += wj * __uint_as_float(pv[j].y & 0xFFFF0000u);
     }
   }
   uint2 pk;
