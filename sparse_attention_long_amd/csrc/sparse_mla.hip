@@ -613,36 +613,61 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
   const float l_tot = sum_halves(rs.l_sum);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (rs.m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (h < a.H) {
+  // The row's output, or with splits this split's normalised output in bf16
+  // (the merge weights sum to 1, so this adds at most one more bf16 rounding
+  // to the result; it halves the partial traffic of the decode step).  Both
+  // are [H][Dv] blocks, so a wave's 32 heads are 32 KB of contiguous memory.
+  uint16_t* const ob = a.nsplit == 1 ? a.out + qrow * a.H * DV
+                                     : a.part_o + ((int64_t)rowid * a.nsplit + sp) * a.H * DV;
+  if constexpr (C::kRowDma) {
+    // Staged through LDS (the ring tiles are free once the row is done:
+    // every copy has landed and the redo check's barriers have passed), so
+    // that each store instruction writes two whole 512-byte head-row halves
+    // rather than 16 bytes of each of 32 rows.  Wave w uses a 16.5 KB
+    // region of tile0 (w < 2) or tile1; rows are padded to 264 elements
+    // (132 dwords) so the 8-byte writes of the 32 heads spread over the
+    // banks.  Half p of the dims goes per pass.
+    constexpr int kHalf = DV / 2, kStride = kHalf + 8;
+    static_assert(2 * 32 * kStride <= C::kTileElems, "two waves' staging fits one tile");
+    uint16_t* stg = (wave < 2 ? tile0 : tile1) + (wave & 1) * 32 * kStride;
+    const int h0 = wave * 32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int t = p * C::kNT / 2; t < (p + 1) * C::kNT / 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * t + 8 * g + 4 * half - p * kHalf;
+          uint2 pk;
+          pk.x = pack_bf16x2(rs.o[t][4 * g + 0] * inv, rs.o[t][4 * g + 1] * inv);
+          pk.y = pack_bf16x2(rs.o[t][4 * g + 2] * inv, rs.o[t][4 * g + 3] * inv);
+          *(uint2*)(stg + col * kStride + d) = pk;
+        }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hh = 2 * i + half;
+        const uint4 v = *(const uint4*)(stg + hh * kStride + 8 * col);
+        if (h0 + hh < a.H) *(uint4*)(ob + (int64_t)(h0 + hh) * DV + p * kHalf + 8 * col) = v;
+      }
+    }
+  } else if (h < a.H) {
+    uint16_t* op = ob + (int64_t)h * DV;
+#pragma unroll
+    for (int t = 0; t < C::kNT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * t + 8 * g + 4 * half;
+        uint2 pk;
+        pk.x = pack_bf16x2(rs.o[t][4 * g + 0] * inv, rs.o[t][4 * g + 1] * inv);
+        pk.y = pack_bf16x2(rs.o[t][4 * g + 2] * inv, rs.o[t][4 * g + 3] * inv);
+        *(uint2*)(op + d) = pk;
+      }
+  }
+  if (h < a.H && half == 0) {
     if (a.nsplit == 1) {
-      uint16_t* op = a.out + (qrow * a.H + h) * DV;
-#pragma unroll
-      for (int t = 0; t < C::kNT; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * t + 8 * g + 4 * half;
-          uint2 pk;
-          pk.x = pack_bf16x2(rs.o[t][4 * g + 0] * inv, rs.o[t][4 * g + 1] * inv);
-          pk.y = pack_bf16x2(rs.o[t][4 * g + 2] * inv, rs.o[t][4 * g + 3] * inv);
-          *(uint2*)(op + d) = pk;
-        }
-      if (a.lse && half == 0) a.lse[qrow * a.H + h] = lse_v;
+      if (a.lse) a.lse[qrow * a.H + h] = lse_v;
     } else {
-      // The split's normalised output in bf16 (the merge weights sum to 1,
-      // so this adds at most one more bf16 rounding to the result) halves
-      // the partial traffic of the decode step.
-      uint16_t* pp = a.part_o + (((int64_t)rowid * a.nsplit + sp) * a.H + h) * DV;
-#pragma unroll
-      for (int t = 0; t < C::kNT; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * t + 8 * g + 4 * half;
-          uint2 pk;
-          pk.x = pack_bf16x2(rs.o[t][4 * g + 0] * inv, rs.o[t][4 * g + 1] * inv);
-          pk.y = pack_bf16x2(rs.o[t][4 * g + 2] * inv, rs.o[t][4 * g + 3] * inv);
-          *(uint2*)(pp + d) = pk;
-        }
-      if (half == 0) a.part_lse[((int64_t)rowid * a.nsplit + sp) * a.H + h] = lse_v;
+      a.part_lse[((int64_t)rowid * a.nsplit + sp) * a.H + h] = lse_v;
     }
   }
 }
