@@ -406,6 +406,43 @@ def test_attention_large_logits_recompute_path_unsplit():
     assert worst <= ATTN_MAX_REL and wlse <= LSE_ABS * 40
 
 
+@pytest.mark.parametrize("heads,rows", [(72, 3), (72, 256), (1, 2), (100, 300)])
+def test_attention_head_counts_not_multiple_of_32(heads, rows):
+    # A wave owns 32 heads, and the output leaves through a per-wave staging
+    # buffer in whole head rows: heads past H must be neither computed into
+    # the output nor stored.  rows < 256 takes the split path (partials and
+    # the combine), rows >= 256 one workgroup per row.  The output sits at
+    # the start of a larger buffer whose tail must stay untouched.
+    wl = W.custom("p4k", n_kv=4096, heads=heads)
+    rs = np.random.RandomState(11 + heads + rows)
+    q = np.stack([W.q_bf16(wl, 0, [i])[0] for i in range(rows)])[None]
+    idx = np.stack([np.sort(rs.choice(4096, 2048, replace=False)).astype(np.int32) for _ in range(rows)])[None]
+    kv = W.kv_bf16_rows(wl, 0, np.arange(wl.n_kv))[None]
+    dims = dsa.Dims.of(wl, n_q=rows, q_pos0=0)
+    n_out = rows * heads * wl.dim_v
+    guard = 64 * wl.dim_v
+    buf = torch.full((n_out + guard,), 0x7F7F, dtype=torch.int16, device="cuda")
+    out = buf[:n_out].view(1, rows, heads, wl.dim_v)
+    lse = torch.zeros((1, rows, heads), dtype=torch.float32, device="cuda")
+    nws = dsa.dsa_attn_workspace_size(dims)
+    assert (nws > 0) == (rows < 256)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_attn(dims, to_dev(q), to_dev(kv), to_dev(idx), wl.sm_scale, out, lse, ws, nws)
+    torch.cuda.synchronize()
+    assert bool(torch.all(buf[n_out:] == 0x7F7F)), "store past the last head"
+    o = bf16_tensor_to_f64(out)
+    l = lse.cpu().numpy()
+    kvf = O.bf16_decode(kv[0])
+    check = sorted(set(range(rows)) if rows <= 8 else {0, 1, 31, 32, 100, rows // 2, rows - 2, rows - 1})
+    worst, worst_lse = 0.0, 0.0
+    for n in check:
+        ref_o, ref_lse = O.sparse_mla_row(O.bf16_decode(q[0, n]), kvf, idx[0, n], wl.sm_scale, wl.dim_v)
+        worst = max(worst, attn_errors(o[0, n], ref_o).max())
+        worst_lse = max(worst_lse, np.abs(l[0, n] - ref_lse).max())
+    _say(f"H={heads} rows={rows} ws={nws}: attention max rel err", worst, "lse", worst_lse, "rows checked", len(check))
+    assert worst <= ATTN_MAX_REL and worst_lse <= LSE_ABS
+
+
 # ----------------------------------------------------------------- fused forward
 def run_forward(wl, d, with_idx=True):
     dims = dsa.Dims.of(wl)
