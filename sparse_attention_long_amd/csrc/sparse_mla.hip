@@ -917,7 +917,7 @@ __global__ void __launch_bounds__(NW * kWave, 1) indexer_kl_kernel(KlArgs ka) {
 
 // Merge split partials: lse = log sum_j exp(lse_j), o = sum_j exp(lse_j - lse) o_j.
 template <int DV>
-__global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(DV / 8) mla_combine_kernel(AttnArgs a) {
   // (row, head) on the XCD that ran the row's splits (rows 8j + x on XCD x)
   const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
   const int rowid = (jw / a.H) * 8 + xcd;
@@ -926,19 +926,20 @@ __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
   const int b = rowid / a.rows, i = rowid % a.rows;
   const int64_t qrow = (int64_t)b * a.qrows_b + i;
   const float* pl = a.part_lse + (int64_t)rowid * a.nsplit * a.H + h;
-  const int d = threadIdx.x * 4;
+  const int d = threadIdx.x * 8;
   const uint16_t* po = a.part_o + ((int64_t)rowid * a.nsplit * a.H + h) * DV + d;
   const int64_t pstride = (int64_t)a.H * DV;
-  // Every split's log-sum-exp and partial are loaded before the first is
-  // used, so a thread waits for one memory round trip, not one per split
-  // (an empty split's partial is zeros, written by the split kernel).
+  // One wave per (row, head), 8 dims per lane in 16-byte loads.  Every
+  // split's log-sum-exp and partial are loaded before the first is used, so
+  // a lane waits for one memory round trip, not one per split (an empty
+  // split's partial is zeros, written by the split kernel).
   float lv[kMaxSplits];
-  uint2 pv[kMaxSplits];
+  uint4 pv[kMaxSplits];
 #pragma unroll
   for (int j = 0; j < kMaxSplits; ++j)
     if (j < a.nsplit) {
       lv[j] = pl[(int64_t)j * a.H];
-      pv[j] = *(const uint2*)(po + j * pstride);
+      pv[j] = *(const uint4*)(po + j * pstride);
     }
   float mx = -INFINITY;
 #pragma unroll
@@ -951,22 +952,26 @@ __global__ void __launch_bounds__(DV / 4) mla_combine_kernel(AttnArgs a) {
       if (j < a.nsplit) den += __expf(lv[j] - mx);
   }
   const float lse = mx > -INFINITY ? mx + __logf(den) : -INFINITY;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (mx > -INFINITY) {
 #pragma unroll
     for (int j = 0; j < kMaxSplits; ++j) {
       if (j >= a.nsplit || lv[j] == -INFINITY) continue;
       const float wj = __expf(lv[j] - lse);
-      acc.x += wj * __uint_as_float(pv[j].x << 16);
-      acc.y += wj * __uint_as_float(pv[j].x & 0xFFFF0000u);
-      acc.z += wj * __uint_as_float(pv[j].y << 16);
-      acc.w += wj * __uint_as_float(pv[j].y & 0xFFFF0000u);
+      const uint32_t w4[4] = {pv[j].x, pv[j].y, pv[j].z, pv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += wj * __uint_as_float(w4[e] << 16);
+        acc[2 * e + 1] += wj * __uint_as_float(w4[e] & 0xFFFF0000u);
+      }
     }
   }
-  uint2 pk;
-  pk.x = pack_bf16x2(acc.x, acc.y);
-  pk.y = pack_bf16x2(acc.z, acc.w);
-  *(uint2*)(a.out + (qrow * a.H + h) * DV + d) = pk;
+  uint4 pk;
+  pk.x = pack_bf16x2(acc[0], acc[1]);
+  pk.y = pack_bf16x2(acc[2], acc[3]);
+  pk.z = pack_bf16x2(acc[4], acc[5]);
+  pk.w = pack_bf16x2(acc[6], acc[7]);
+  *(uint4*)(a.out + (qrow * a.H + h) * DV + d) = pk;
   if (a.lse && threadIdx.x == 0) a.lse[qrow * a.H + h] = lse;
 }
 
@@ -980,7 +985,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((sparse_mla_kernel<DK, DV, NW, false>), dim3(grid), dim3(NW * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3((unsigned)(8 * nrow8 * a.H)), dim3(DV / 4), 0, st, a);
+  hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3((unsigned)(8 * nrow8 * a.H)), dim3(DV / 8), 0, st, a);
   return hipGetLastError();
 }
 
