@@ -492,15 +492,29 @@ __global__ void __launch_bounds__(NW * kWave, 1) sparse_mla_kernel(AttnArgs a) {
 
   // Slot j holds the cache row of its token (-1 if the entry is padding or
   // outside the sequence): a row of the sequence's cache, or of the pool.
+  // A thread's (at most kMaxSlots / kThreads) index loads all go out before
+  // the first is used, so the prologue waits for one memory round trip (two
+  // with a page table) rather than one per slot a thread covers.
   const int slen = seq_len_of(a.pk, b, a.S);
-  for (int j = threadIdx.x; j < nchunks * kChunk; j += C::kThreads) {
-    int v = -1;
-    if (j < nslots) {
-      v = a.idx[((int64_t)b * a.idx_rows_b + i) * a.k + slot0 + j];
-      if (v < 0 || v >= slen) v = -1;
-      else if (kPaged) v = (int)cache_row(a.pk, b, a.S, v);
+  {
+    constexpr int kPer = kMaxSlots / C::kThreads;
+    const int32_t* ip = a.idx + ((int64_t)b * a.idx_rows_b + i) * a.k + slot0;
+    int v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = (int)threadIdx.x + u * C::kThreads;
+      v[u] = j < nslots ? ip[j] : -1;
     }
-    sidx[j] = v;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (v[u] < 0 || v[u] >= slen) v[u] = -1;
+      else if (kPaged) v[u] = (int)cache_row(a.pk, b, a.S, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = (int)threadIdx.x + u * C::kThreads;
+      if (j < nchunks * kChunk) sidx[j] = v[u];
+    }
   }
 
   __syncthreads();   // the slot indices are published
@@ -750,18 +764,32 @@ __global__ void __launch_bounds__(NW * kWave, 1) indexer_kl_kernel(KlArgs ka) {
   // slots: cache rows (or -1) and the index scores of their tokens
   const int slen = seq_len_of(a.pk, b, a.S);
   const float* srow = ka.scores + ((int64_t)b * ka.sc_rows_b + i) * ka.ld;
-  for (int j = threadIdx.x; j < nchunks * kChunk; j += C::kThreads) {
-    int v = -1;
-    float iv = -INFINITY;
-    if (j < a.k) {
-      const int t = a.idx[((int64_t)b * a.idx_rows_b + i) * a.k + j];
-      if (t >= 0 && t < slen) {
-        iv = srow[t];
-        v = kPaged ? (int)cache_row(a.pk, b, a.S, t) : t;
+  {
+    // all of a thread's index loads first, then all of its score loads
+    constexpr int kPer = kMaxSlots / C::kThreads;
+    const int32_t* ip = a.idx + ((int64_t)b * a.idx_rows_b + i) * a.k;
+    int t[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = (int)threadIdx.x + u * C::kThreads;
+      t[u] = j < a.k ? ip[j] : -1;
+    }
+    int v[kPer];
+    float iv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const bool ok = t[u] >= 0 && t[u] < slen;
+      iv[u] = ok ? srow[t[u]] : -INFINITY;
+      v[u] = !ok ? -1 : kPaged ? (int)cache_row(a.pk, b, a.S, t[u]) : t[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = (int)threadIdx.x + u * C::kThreads;
+      if (j < nchunks * kChunk) {
+        sidx[j] = v[u];
+        isc[j] = iv[u];
       }
     }
-    sidx[j] = v;
-    isc[j] = iv;
   }
   __syncthreads();
   // LSE_I over the selected set: block max, then block sum (fixed orders)
